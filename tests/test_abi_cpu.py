@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/trsm.h declares, rejects bad arguments before any HIP call, and takes
+the quick returns (m == 0, n == 0, batch == 0) without touching the device."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+
+
+def header_functions():
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(INCLUDE, h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(trsm_[a-z_]+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def T():
+    import triangular_solve_trsm_amd as T
+    return T
+
+
+def test_header_declares_expected_entry_points(T):
+    assert header_functions() == sorted(T.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(T):
+    for name in header_functions():
+        assert hasattr(T.lib, name), name
+    # and they are real dynamic symbols of the shared object
+    lib = ctypes.CDLL(T.LIB_PATH)
+    for name in header_functions():
+        getattr(lib, name)
+
+
+def test_status_strings(T):
+    for code, text in [(0, "success"), (1, "invalid value"), (2, "workspace allocation failed"),
+                       (3, "HIP runtime error"), (4, "not supported"), (99, "unknown status")]:
+        assert T.trsm_status_string(code) == text
+
+
+def test_select_ib_table(T):
+    for dt in (T.R32F, T.R64F, T.C64F):
+        for m in (1, 65, 500, 1000, 4096, 8192, 100000):
+            assert T.trsm_lln_select_ib(dt, m, m) in T.IB_CHOICES
+    assert T.trsm_lln_select_ib(7, 100, 100) == 0
+    assert T.trsm_lln_select_ib(T.R64F, -1, 5) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below returns before any HIP call
+
+
+def call(T, dtype=1, m=4, n=3, alpha=1.0, A=FAKE, lda=4, B=FAKE, ldb=4):
+    al = T.alpha_buffer(dtype if dtype in (0, 1, 2) else 1, alpha)
+    return T.lib.trsm_lln(dtype, m, n, ctypes.addressof(al), A, lda, B, ldb, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(dtype=3), dict(dtype=-1), dict(m=-1), dict(n=-2), dict(lda=3), dict(ldb=3),
+    dict(m=0, lda=0), dict(A=None), dict(B=None), dict(m=5, lda=4, ldb=5), dict(m=5, lda=5, ldb=4),
+])
+def test_invalid_arguments(T, kw):
+    assert call(T, **kw) == 1
+
+
+def test_null_alpha_invalid(T):
+    assert T.lib.trsm_lln(1, 4, 3, None, FAKE, 4, FAKE, 4, None) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(m=0, lda=1, ldb=1), dict(n=0), dict(m=0, n=0, lda=1, ldb=1)])
+def test_quick_return_without_device(T, kw):
+    # null pointers are allowed when m*n == 0
+    kw2 = dict(kw, A=None, B=None)
+    assert call(T, **kw2) == 0
+
+
+def test_batched_argument_checks(T):
+    al = T.alpha_buffer(1, 1.0)
+    f = T.lib.trsm_lln_strided_batched
+    a = ctypes.addressof(al)
+    assert f(1, 4, 3, a, FAKE, 4, 16, FAKE, 4, 12, -1, None) == 1      # batch < 0
+    assert f(1, 4, 3, a, FAKE, 4, -16, FAKE, 4, 12, 2, None) == 1      # negative stride
+    assert f(1, 4, 3, a, FAKE, 3, 16, FAKE, 4, 12, 2, None) == 1       # lda < m
+    assert f(1, 4, 3, a, FAKE, 4, 16, FAKE, 4, 12, 0, None) == 0       # batch == 0
+    assert f(1, 0, 3, a, None, 1, 0, None, 1, 0, 5, None) == 0         # m == 0
+
+
+def test_ex_rejects_bad_block_size(T):
+    al = T.alpha_buffer(1, 1.0)
+    a = ctypes.addressof(al)
+    for ib in (1, 32, 100, 1024, -64):
+        assert T.lib.trsm_lln_ex(1, 100, 3, a, FAKE, 100, FAKE, 100, ib, 0, None) == 1
+    # valid block size, quick return
+    assert T.lib.trsm_lln_ex(1, 100, 0, a, FAKE, 100, FAKE, 100, 128, 0, None) == 0
+
+
+def test_python_binding_rejects_bad_layouts(T):
+    import torch
+    A = torch.zeros(4, 4, dtype=torch.float64)
+    B = torch.zeros(4, 3, dtype=torch.float64)       # row-major: stride(0) != 1
+    with pytest.raises(ValueError):
+        T.trsm_lln(A.T, B, 1.0)
+    with pytest.raises(TypeError):
+        T.trsm_lln(A.T, torch.zeros(3, 4, dtype=torch.int32).T, 1.0)
+    with pytest.raises(ValueError):
+        T.trsm_lln(torch.zeros(5, 5, dtype=torch.float64).T, torch.zeros(3, 4, dtype=torch.float64).T)
+
+
+def test_kernel_entry_points_reject_bad_arguments(T):
+    one = T.alpha_buffer(1, 1.0)
+    zero = T.alpha_buffer(1, 0.0)
+    a1, a0 = ctypes.addressof(one), ctypes.addressof(zero)
+    f = T.lib.trsm_kernel_diag_inv
+    assert f(1, 100, 10, FAKE, 10, FAKE, None) == 1       # ib not a candidate
+    assert f(1, 64, 10, FAKE, 9, FAKE, None) == 1         # lda < m
+    assert f(9, 64, 10, FAKE, 10, FAKE, None) == 1        # dtype
+    assert f(1, 64, 0, None, 1, None, None) == 0          # m == 0
+    g = T.lib.trsm_kernel_gemm
+    #         dt M  N  K  beta gamma A    lda B    ldb C    ldc D    ldd D2   ldd2 split low
+    assert g(1, 8, 4, 6, a0, a1, FAKE, 7, FAKE, 6, None, 8, FAKE, 8, None, 8, 0, 0, None) == 1  # lda < M
+    assert g(1, 8, 4, 6, a0, a1, FAKE, 8, FAKE, 5, None, 8, FAKE, 8, None, 8, 0, 0, None) == 1  # ldb < K
+    assert g(1, 8, 4, 6, a1, a1, FAKE, 8, FAKE, 6, None, 8, FAKE, 8, None, 8, 0, 0, None) == 1  # beta != 0, C null
+    assert g(1, 8, 4, 6, a0, a1, FAKE, 8, FAKE, 6, None, 8, FAKE, 8, None, 8, 0, 1, None) == 1  # a_lower, M != K
+    assert g(1, 8, 4, 8, a0, a1, FAKE, 8, FAKE, 8, None, 8, FAKE, 8, FAKE, 8, 9, 0, None) == 1  # split > M
+    assert g(1, 8, 4, 8, a0, a1, FAKE, 8, FAKE, 8, None, 8, FAKE, 8, FAKE, 3, 4, 0, None) == 1  # ldd2 < split
+    assert g(1, 0, 4, 8, a0, a1, None, 1, FAKE, 8, None, 1, None, 1, None, 1, 0, 0, None) == 0  # M == 0
+
+
+def test_profiler_bookkeeping_without_launches(T):
+    T.trsm_profile_start()
+    assert T.trsm_profile_count() == 0
+    T.trsm_profile_stop()
+    with pytest.raises(T.TrsmError):
+        T.trsm_profile_read(0)

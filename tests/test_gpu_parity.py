@@ -1,0 +1,260 @@
+"""Parity of the HIP library with the CPU oracle on the GPU.
+
+Every case calls the C ABI through the Python binding and compares with the
+oracle element by element: normwise relative error <= 1e-12 (fp64, complex
+fp64) or <= 1e-4 (fp32), the bar fixed for this operation.  Well-conditioned
+inputs put correct results near 1e-16 / 1e-7 (the pages' Table 2 scale); a
+sanity bound of 1e-13 / 1e-5 is checked as well so that a result near the
+tolerance (a sign of a bug) does not pass silently.
+
+Full-size workloads are checked on sampled right-hand-side columns (columns
+are independent: column j of X depends only on L and column j of B) and, on
+the whole output, by the residual property ||L X - alpha B|| that holds at
+any size.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import TOL, from_dev, ld_of, max_problem_nrel, nrel, to_dev, torch_dtype
+from trsm_inputs import CONFIGS, make_config, make_problem, small_integer_rhs, unit_bidiagonal_minus_one
+
+pytestmark = pytest.mark.gpu
+
+SANITY = {"f32": 1e-5, "f64": 1e-13, "c64": 1e-13}
+
+
+@pytest.fixture(scope="module")
+def T():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import triangular_solve_trsm_amd as T
+    return T
+
+
+def sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def solve_gpu(T, L, B, alpha, **kw):
+    Ad = to_dev(L)
+    Bd = to_dev(B)
+    if kw:
+        T.trsm_lln_ex(Ad, Bd, alpha, **kw)
+    else:
+        T.trsm_lln(Ad, Bd, alpha)
+    sync()
+    return from_dev(Bd)
+
+
+def check(dtype, X, ref, what=""):
+    e = nrel(X, ref)
+    assert e <= TOL[dtype], f"{what}: error {e:.3e} > {TOL[dtype]}"
+    assert e <= SANITY[dtype], f"{what}: error {e:.3e} is within tolerance but far above rounding"
+    return e
+
+
+# ---- the five workloads ----------------------------------------------------
+
+def test_c1_single_f64_64(T):
+    cfg = CONFIGS["c1_f64_64"]
+    L, B, a = make_config(cfg)
+    check("f64", solve_gpu(T, L, B, a), oracle.solve(L, B, a), cfg.name)
+
+
+def test_c2_batched_c64_64(T):
+    cfg = CONFIGS["c2_c64_64x64_b8192"]
+    L, B, a = make_config(cfg)
+    Ad, Bd = to_dev(L), to_dev(B)
+    T.trsm_lln_strided_batched(Ad, Bd, a)
+    sync()
+    X = from_dev(Bd)
+    ref = oracle.solve_batched(L, B, a)
+    e = max_problem_nrel(X, ref)
+    assert e <= TOL["c64"] and e <= SANITY["c64"], e
+
+
+@pytest.mark.parametrize("name", ["c3_f32_4096", "c4_f64_8192", "c5_c64_8192x2048"])
+def test_large_workloads_sampled_and_residual(T, name):
+    import torch
+    cfg = CONFIGS[name]
+    L, B, a = make_config(cfg)
+    Ad, Bd = to_dev(L), to_dev(B)
+    B0 = Bd.clone()
+    T.trsm_lln(Ad, Bd, a)
+    sync()
+    cols = np.unique(np.linspace(0, cfg.n - 1, 8).astype(int))
+    Xs = from_dev(Bd[:, torch.as_tensor(cols, device=Bd.device)])
+    ref = oracle.solve(L, np.asfortranarray(B[:, cols]), a)
+    check(cfg.dtype, Xs, ref, name)
+    # residual of the whole output, computed on the GPU in float64/complex128
+    wide = torch.complex128 if cfg.dtype == "c64" else torch.float64
+    Lw = torch.tril(Ad.to(wide))
+    Xw, Bw = Bd.to(wide), B0.to(wide)
+    R = Lw @ Xw - a * Bw
+    res = (torch.linalg.norm(R) / (torch.linalg.norm(Lw) * torch.linalg.norm(Xw)
+                                   + abs(a) * torch.linalg.norm(Bw))).item()
+    u = 2.0 ** -24 if cfg.dtype == "f32" else 2.0 ** -53
+    assert res <= 10 * cfg.m * u, res
+
+
+# ---- regime edges, ragged blocks, layouts ----------------------------------
+
+EDGE_M = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129]
+EDGE_N = [1, 5, 64, 65, 130]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+def test_regime_edges(T, dtype):
+    worst = 0.0
+    for m in EDGE_M:
+        for n in EDGE_N:
+            L, B = make_problem(dtype, m, n, seed=1000 + 7 * m + n)
+            a = 0.5 - 0.25j if dtype == "c64" else 0.5
+            X = solve_gpu(T, L, B, a)
+            worst = max(worst, check(dtype, X, oracle.solve(L, B, a), f"{dtype} m={m} n={n}"))
+    print(f"{dtype} regime edges: worst error {worst:.2e}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("ib", [64, 128, 256, 512])
+def test_every_block_size_ragged(T, dtype, ib):
+    """m = 1000 is a multiple of no candidate block size; n = 257 is ragged
+    against the GEMM tiles."""
+    m, n = 1000, 257
+    L, B = make_problem(dtype, m, n, seed=ib)
+    a = 0.75 + 0.5j if dtype == "c64" else 0.75
+    X = solve_gpu(T, L, B, a, ib=ib)
+    check(dtype, X, oracle.solve(L, B, a), f"{dtype} ib={ib}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+def test_m_4097_narrow(T, dtype):
+    m, n = 4097, 19
+    L, B = make_problem(dtype, m, n, seed=4097)
+    X = solve_gpu(T, L, B, 1.0)
+    check(dtype, X, oracle.solve(L, B, 1.0), f"{dtype} m=4097")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("m,n", [(50, 40), (700, 90)])
+def test_padding_and_poisoned_upper_triangle(T, dtype, m, n):
+    """A's strict upper triangle and its padding rows hold NaN and must not
+    matter; B's padding rows must be left untouched."""
+    L, B = make_problem(dtype, m, n, seed=m + n, lda=m + 13, ldb=m + 5, upper="nan")
+    Ad = to_dev(L, pad=np.nan)
+    Bd = to_dev(B, pad=12345.0)
+    T.trsm_lln(Ad, Bd, 1.0)
+    sync()
+    import torch
+    full = from_dev(torch.as_strided(Bd, (ld_of(B), n), (1, ld_of(B))))
+    assert np.all(full[m:] == 12345.0), "padding rows of B were modified"
+    Lz, _ = make_problem(dtype, m, n, seed=m + n)
+    check(dtype, full[:m], oracle.solve(Lz, np.asfortranarray(B), 1.0), f"{dtype} padded")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+def test_force_blocked_small_sizes(T, dtype):
+    for m in (1, 17, 64):
+        L, B = make_problem(dtype, m, 33, seed=m)
+        X = solve_gpu(T, L, B, 2.0, ib=64, force_blocked=True)
+        check(dtype, X, oracle.solve(L, B, 2.0), f"{dtype} blocked m={m}")
+
+
+# ---- batches -----------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("batch,m,n", [(1, 64, 64), (7, 33, 70), (7, 64, 64), (3, 150, 20)])
+def test_batched(T, dtype, batch, m, n):
+    L, B = make_problem(dtype, m, n, seed=batch * 100 + m, batch=batch)
+    a = 0.5 - 0.25j if dtype == "c64" else -0.5
+    Ad, Bd = to_dev(L), to_dev(B)
+    T.trsm_lln_strided_batched(Ad, Bd, a)
+    sync()
+    X = from_dev(Bd)
+    ref = oracle.solve_batched(L, B, a)
+    e = max_problem_nrel(X, ref)
+    assert e <= TOL[dtype] and e <= SANITY[dtype], e
+
+
+# ---- special values and exact cases ------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("m", [40, 300])
+def test_alpha_zero_zeroes_B_without_reading_A(T, dtype, m):
+    import torch
+    _, B = make_problem(dtype, m, 9, seed=2)
+    Ad = to_dev(np.full((m, m), np.nan, dtype=B.dtype, order="F"))
+    Bd = to_dev(B)
+    T.trsm_lln(Ad, Bd, 0.0)
+    sync()
+    assert torch.all(Bd == 0).item()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("m,ib", [(64, 0), (600, 128), (1000, 256)])
+def test_bidiagonal_exact(T, dtype, m, ib):
+    """Unit bidiagonal L with -1 below the diagonal: X is the running sum of
+    B down each column, exact for integer B on every path (the inverse of
+    each diagonal block is the all-ones lower triangle, also exact)."""
+    L = unit_bidiagonal_minus_one(m, dtype)
+    B = small_integer_rhs(m, 70, dtype, seed=m)
+    X = solve_gpu(T, L, B, 1.0, ib=ib) if ib else solve_gpu(T, L, B, 1.0)
+    assert np.array_equal(X, np.cumsum(B, axis=0)), f"{dtype} m={m}"
+
+
+@pytest.mark.parametrize("dtype", ["f64", "c64"])
+def test_deterministic(T, dtype):
+    L, B = make_problem(dtype, 900, 300, seed=5)
+    X1 = solve_gpu(T, L, B, 1.0)
+    X2 = solve_gpu(T, L, B, 1.0)
+    assert np.array_equal(X1, X2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+def test_error_scale_vs_pages_table2(T, dtype):
+    """At m = n = 1024 the GPU-vs-oracle error is of the order the pages
+    report against a vendor TRSM (Table 2), at most 10x that figure."""
+    import json
+    here = os.path.dirname(os.path.abspath(__file__))
+    table = json.load(open(os.path.join(here, "golden", "table2_normwise_error.json")))
+    ref_err = table["error"][dtype][table["sizes"].index(1024)]
+    L, B = make_problem(dtype, 1024, 1024, seed=1024)
+    e = nrel(solve_gpu(T, L, B, 1.0), oracle.solve(L, B, 1.0))
+    assert e <= 10 * ref_err, (dtype, e, ref_err)
+
+
+def test_non_default_stream(T):
+    import torch
+    L, B = make_problem("f64", 500, 100, seed=3)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Ad, Bd = to_dev(L), to_dev(B)
+        T.trsm_lln(Ad, Bd, 1.0, stream=s)
+    s.synchronize()
+    check("f64", from_dev(Bd), oracle.solve(L, B, 1.0), "side stream")
+
+
+def test_workspace_allocation_failure_leaves_B_untouched(T, monkeypatch):
+    import torch
+    L, B = make_problem("f64", 300, 40, seed=9)
+    s = torch.cuda.Stream()  # fresh stream: its workspace is not cached yet
+    with torch.cuda.stream(s):
+        Ad, Bd = to_dev(L), to_dev(B)
+    s.synchronize()
+    monkeypatch.setenv("TRSM_FAIL_ALLOC", "1")
+    with pytest.raises(T.TrsmError) as ei:
+        T.trsm_lln(Ad, Bd, 1.0, stream=s)
+    assert ei.value.status == 2
+    monkeypatch.delenv("TRSM_FAIL_ALLOC")
+    s.synchronize()
+    assert np.array_equal(from_dev(Bd), B)
+    T.trsm_lln(Ad, Bd, 1.0, stream=s)
+    s.synchronize()
+    check("f64", from_dev(Bd), oracle.solve(L, B, 1.0), "after failed alloc")
+    T.trsm_release_workspace()

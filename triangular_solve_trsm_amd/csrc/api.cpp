@@ -1,0 +1,506 @@
+// C ABI of the library: argument checks, regime dispatch, the blocked
+// driver (phase 2 loop) and the per-(device, stream) workspace cache.
+//
+// Dispatch follows the hierarchical framework of HSMA-TRSM ("Hierarchical
+// Shared Memory-Aware Optimization for TRSM on GPU Platforms", section 4.1,
+// Figure 2): m <= 64 takes the direct solve (kernel a); larger m takes the
+// blocked algorithm of section 4.3 with the block size from the offline
+// table of section 4.3.2.
+//
+// Blocked driver (section 4.3, right-looking form of phase 2):
+//   phase 1:  W_t = D_t^{-1} for every diagonal block, one launch;
+//   copy B_0 -> P (panel buffer, ld = ib);
+//   for r = 0 .. nb-1:
+//     solve:   B_r = g_r * W_r * P          (g_0 = alpha, else 1; triangular W)
+//     update:  rows below block r:  beta_r * B_{r+1:} - L_{r+1:, r} * B_r,
+//              with beta_0 = alpha, else 1; the rows of block r+1 are written
+//              to P (the next solve's input), the rest in place.
+// The pages state the update left-looking (B_r -= A_{r,[0:r]} X_{[0:r]});
+// the right-looking order computes the same sums with one GEMM of K = ib per
+// block row, whose M x N extent keeps all 256 CUs busy early on.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "trsm.h"
+#include "trsm_internal.h"
+#include "trsm_kernels.h"
+#include <vector>
+
+using namespace trsm;
+
+namespace {
+
+struct IbEntry {
+    int dtype;
+    int64_t m;
+    int ib;
+};
+#include "ib_table.inc"
+
+bool log_enabled() {
+    static const bool on = [] {
+        const char *e = std::getenv("TRSM_LOG");
+        return e && e[0] == '1';
+    }();
+    return on;
+}
+
+// ---- device checks and workspace cache ----------------------------------
+
+std::mutex g_mu;
+std::map<int, bool> g_dev_ok;                                  // device -> is gfx950
+std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
+
+trsm_status_t check_device(int *dev_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+    *dev_out = dev;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_dev_ok.find(dev);
+    if (it == g_dev_ok.end()) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+        const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+        it = g_dev_ok.emplace(dev, ok).first;
+    }
+    return it->second ? TRSM_STATUS_SUCCESS : TRSM_STATUS_NOT_SUPPORTED;
+}
+
+trsm_status_t get_workspace(int dev, hipStream_t st, size_t bytes, void **out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto &e = g_ws[{dev, st}];
+    if (e.second < bytes) {
+        if (e.first) {
+            if (hipStreamSynchronize(st) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+            (void)hipFree(e.first);
+            e.first = nullptr;
+            e.second = 0;
+        }
+        const char *fail = std::getenv("TRSM_FAIL_ALLOC");  // test hook
+        if (fail && fail[0] == '1') return TRSM_STATUS_ALLOC_FAILED;
+        void *p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return TRSM_STATUS_ALLOC_FAILED;
+        }
+        e.first = p;
+        e.second = bytes;
+    }
+    *out = e.first;
+    return TRSM_STATUS_SUCCESS;
+}
+
+// ---- launch profiling ----------------------------------------------------
+
+struct ProfRec {
+    trsm_profile_record_t r;
+    hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Records HIP events around one launch on `st` while profiling is on.
+class LaunchTimer {
+  public:
+    LaunchTimer(int kind, int dt, int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t st)
+        : st_(st) {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (!g_prof_on) return;
+        rec_.r = trsm_profile_record_t{kind, dt, m, n, k, batch, 0.0f};
+        rec_.start = take_event();
+        rec_.stop = take_event();
+        if (rec_.start && rec_.stop && hipEventRecord(rec_.start, st_) == hipSuccess) active_ = true;
+    }
+    ~LaunchTimer() {
+        if (!active_) return;
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (hipEventRecord(rec_.stop, st_) == hipSuccess) g_prof.push_back(rec_);
+    }
+
+  private:
+    hipStream_t st_;
+    ProfRec rec_{};
+    bool active_ = false;
+};
+
+// ---- argument handling --------------------------------------------------
+
+bool valid_dtype(int dt) { return dt == TRSM_R32F || dt == TRSM_R64F || dt == TRSM_C64F; }
+
+Scalar read_alpha(int dt, const void *alpha) {
+    Scalar s{0.0, 0.0};
+    if (dt == TRSM_R32F) s.re = *static_cast<const float *>(alpha);
+    else if (dt == TRSM_R64F) s.re = *static_cast<const double *>(alpha);
+    else {
+        const double *a = static_cast<const double *>(alpha);
+        s.re = a[0];
+        s.im = a[1];
+    }
+    return s;
+}
+
+trsm_status_t check_args(int dt, int64_t m, int64_t n, const void *alpha, const void *A,
+                         int64_t lda, const void *B, int64_t ldb) {
+    if (!valid_dtype(dt)) return TRSM_STATUS_INVALID_VALUE;
+    if (m < 0 || n < 0) return TRSM_STATUS_INVALID_VALUE;
+    const int64_t mn1 = m > 1 ? m : 1;
+    if (lda < mn1 || ldb < mn1) return TRSM_STATUS_INVALID_VALUE;
+    if (m > 0 && n > 0 && (A == nullptr || B == nullptr || alpha == nullptr))
+        return TRSM_STATUS_INVALID_VALUE;
+    // element offsets must fit in int64 (the kernels index with int64)
+    if (m > 0 && n > 0 && (ldb > INT64_MAX / n || lda > INT64_MAX / m)) return TRSM_STATUS_INVALID_VALUE;
+    return TRSM_STATUS_SUCCESS;
+}
+
+trsm_status_t hip_status(hipError_t e) { return e == hipSuccess ? TRSM_STATUS_SUCCESS : TRSM_STATUS_HIP_ERROR; }
+
+int select_ib(int dt, int64_t m) {
+    int best = 256;
+    int64_t bestd = INT64_MAX;
+    for (const IbEntry &e : kIbTable) {
+        if (e.dtype != dt) continue;
+        const int64_t d = e.m > m ? e.m - m : m - e.m;
+        if (d < bestd) {
+            bestd = d;
+            best = e.ib;
+        }
+    }
+    return best;
+}
+
+// Blocked path for one problem (m > 0, n > 0, alpha != 0).
+trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void *A,
+                          int64_t lda, void *B, int64_t ldb, int ib, int dev, hipStream_t st) {
+    const size_t es = dtype_size(dt);
+    const int64_t nb = (m + ib - 1) / ib;
+    size_t wbytes = (size_t)nb * ib * ib * es;
+    wbytes = (wbytes + 255) & ~(size_t)255;
+    const size_t pbytes = (size_t)ib * n * es;
+    void *ws = nullptr;
+    trsm_status_t s = get_workspace(dev, st, wbytes + pbytes, &ws);
+    if (s != TRSM_STATUS_SUCCESS) return s;
+    char *W = static_cast<char *>(ws);
+    void *P = W + wbytes;
+    const char *Ab = static_cast<const char *>(A);
+    char *Bb = static_cast<char *>(B);
+    if (log_enabled())
+        std::fprintf(stderr, "[trsm] blocked dtype=%d m=%lld n=%lld ib=%d nb=%lld\n", dt,
+                     (long long)m, (long long)n, ib, (long long)nb);
+
+    hipError_t e;
+    {
+        LaunchTimer t(TRSM_KERNEL_DIAG_INV, dt, m, ib, 0, nb, st);
+        e = diag_inv_launch(dt, ib, m, A, lda, W, st);
+    }
+    if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+    const int64_t bs0 = m < ib ? m : ib;
+    {
+        LaunchTimer t(TRSM_KERNEL_COPY, dt, bs0, n, 0, 1, st);
+        e = copy_panel_launch(dt, bs0, n, B, ldb, P, ib, st);
+    }
+    if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+    const Scalar one{1.0, 0.0};
+    const Scalar minus_one{-1.0, 0.0};
+    for (int64_t r = 0; r < nb; ++r) {
+        const int64_t r0 = r * ib;
+        const int64_t bs = (m - r0) < ib ? (m - r0) : ib;
+        // solve: B_r = g_r * W_r * P
+        GemmDesc sg{};
+        sg.M = bs;
+        sg.N = n;
+        sg.K = bs;
+        sg.A = W + (size_t)r * ib * ib * es;
+        sg.lda = ib;
+        sg.Bm = P;
+        sg.ldb = ib;
+        sg.C = nullptr;
+        sg.ldc = ldb;
+        sg.D = Bb + (size_t)r0 * es;
+        sg.ldd = ldb;
+        sg.D2 = nullptr;
+        sg.ldd2 = ldb;
+        sg.split = 0;
+        sg.beta = Scalar{0.0, 0.0};
+        sg.gamma = (r == 0) ? alpha : one;
+        sg.a_lower = 1;
+        {
+            LaunchTimer t(TRSM_KERNEL_SOLVE_GEMM, dt, bs, n, bs, 1, st);
+            e = gemm_launch(dt, sg, st);
+        }
+        if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+        if (r + 1 == nb) break;
+        // update: rows below block r
+        const int64_t mrest = m - r0 - bs;
+        const int64_t bsn = mrest < ib ? mrest : ib;
+        GemmDesc ug{};
+        ug.M = mrest;
+        ug.N = n;
+        ug.K = bs;
+        ug.A = Ab + ((size_t)(r0 + bs) + (size_t)r0 * lda) * es;
+        ug.lda = lda;
+        ug.Bm = Bb + (size_t)r0 * es;
+        ug.ldb = ldb;
+        ug.C = Bb + (size_t)(r0 + bs) * es;
+        ug.ldc = ldb;
+        ug.D = Bb + (size_t)(r0 + bs) * es;
+        ug.ldd = ldb;
+        ug.D2 = P;
+        ug.ldd2 = ib;
+        ug.split = bsn;
+        ug.beta = (r == 0) ? alpha : one;
+        ug.gamma = minus_one;
+        ug.a_lower = 0;
+        {
+            LaunchTimer t(TRSM_KERNEL_UPDATE_GEMM, dt, mrest, n, bs, 1, st);
+            e = gemm_launch(dt, ug, st);
+        }
+        if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+    }
+    return TRSM_STATUS_SUCCESS;
+}
+
+trsm_status_t run(int dt, int64_t m, int64_t n, const void *alpha_p, const void *A, int64_t lda,
+                  int64_t sA, void *B, int64_t ldb, int64_t sB, int64_t batch, int ib_forced,
+                  bool force_blocked, hipStream_t st) {
+    if (m == 0 || n == 0 || batch == 0) return TRSM_STATUS_SUCCESS;
+    int dev = 0;
+    trsm_status_t s = check_device(&dev);
+    if (s != TRSM_STATUS_SUCCESS) return s;
+    const Scalar alpha = read_alpha(dt, alpha_p);
+    if (alpha.re == 0.0 && alpha.im == 0.0) {
+        if (log_enabled()) std::fprintf(stderr, "[trsm] alpha == 0: B <- 0\n");
+        LaunchTimer t(TRSM_KERNEL_FILL, dt, m, n, 0, batch, st);
+        return hip_status(fill_zero_launch(dt, m, n, B, ldb, sB, batch, st));
+    }
+    if (m <= 64 && !force_blocked) {
+        if (log_enabled())
+            std::fprintf(stderr, "[trsm] small dtype=%d m=%lld n=%lld batch=%lld\n", dt,
+                         (long long)m, (long long)n, (long long)batch);
+        LaunchTimer t(TRSM_KERNEL_SMALL, dt, m, n, 0, batch, st);
+        return hip_status(small_lln_launch(dt, (int)m, n, alpha, A, lda, sA, B, ldb, sB, batch, st));
+    }
+    const int ib = ib_forced ? ib_forced : select_ib(dt, m);
+    const size_t es = dtype_size(dt);
+    for (int64_t p = 0; p < batch; ++p) {
+        s = run_blocked(dt, m, n, alpha, static_cast<const char *>(A) + (size_t)(p * sA) * es, lda,
+                        static_cast<char *>(B) + (size_t)(p * sB) * es, ldb, ib, dev, st);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+    }
+    return TRSM_STATUS_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+trsm_status_t trsm_lln(trsm_dtype_t dtype, int64_t m, int64_t n, const void *alpha,
+                       const void *A, int64_t lda, void *B, int64_t ldb, hipStream_t stream) {
+    try {
+        trsm_status_t s = check_args(dtype, m, n, alpha, A, lda, B, ldb);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        return run(dtype, m, n, alpha, A, lda, 0, B, ldb, 0, 1, 0, false, stream);
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
+trsm_status_t trsm_lln_strided_batched(trsm_dtype_t dtype, int64_t m, int64_t n,
+                                       const void *alpha, const void *A, int64_t lda,
+                                       int64_t strideA, void *B, int64_t ldb, int64_t strideB,
+                                       int64_t batch, hipStream_t stream) {
+    try {
+        if (batch < 0 || strideA < 0 || strideB < 0) return TRSM_STATUS_INVALID_VALUE;
+        trsm_status_t s = check_args(dtype, m, n, alpha, A, lda, B, ldb);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        if (batch > 1 && m > 0 && n > 0 &&
+            (strideA > INT64_MAX / batch || strideB > INT64_MAX / batch))
+            return TRSM_STATUS_INVALID_VALUE;
+        return run(dtype, m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, 0, false, stream);
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
+trsm_status_t trsm_lln_ex(trsm_dtype_t dtype, int64_t m, int64_t n, const void *alpha,
+                          const void *A, int64_t lda, void *B, int64_t ldb, int ib,
+                          int force_blocked, hipStream_t stream) {
+    try {
+        if (ib != 0 && ib != 64 && ib != 128 && ib != 256 && ib != 512)
+            return TRSM_STATUS_INVALID_VALUE;
+        trsm_status_t s = check_args(dtype, m, n, alpha, A, lda, B, ldb);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        return run(dtype, m, n, alpha, A, lda, 0, B, ldb, 0, 1, ib, force_blocked != 0, stream);
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
+trsm_status_t trsm_kernel_diag_inv(trsm_dtype_t dtype, int ib, int64_t m, const void *A,
+                                   int64_t lda, void *W, hipStream_t stream) {
+    try {
+        if (!valid_dtype(dtype) || m < 0 || lda < (m > 1 ? m : 1)) return TRSM_STATUS_INVALID_VALUE;
+        if (ib != 64 && ib != 128 && ib != 256 && ib != 512) return TRSM_STATUS_INVALID_VALUE;
+        if (m == 0) return TRSM_STATUS_SUCCESS;
+        if (A == nullptr || W == nullptr) return TRSM_STATUS_INVALID_VALUE;
+        int dev = 0;
+        trsm_status_t s = check_device(&dev);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        LaunchTimer t(TRSM_KERNEL_DIAG_INV, dtype, m, ib, 0, (m + ib - 1) / ib, stream);
+        return hip_status(diag_inv_launch(dtype, ib, m, A, lda, W, stream));
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
+trsm_status_t trsm_kernel_gemm(trsm_dtype_t dtype, int64_t M, int64_t N, int64_t K,
+                               const void *beta, const void *gamma, const void *A,
+                               int64_t lda, const void *Bm, int64_t ldb, const void *C,
+                               int64_t ldc, void *D, int64_t ldd, void *D2, int64_t ldd2,
+                               int64_t split, int a_lower, hipStream_t stream) {
+    try {
+        if (!valid_dtype(dtype) || M < 0 || N < 0 || K < 0) return TRSM_STATUS_INVALID_VALUE;
+        if (beta == nullptr || gamma == nullptr) return TRSM_STATUS_INVALID_VALUE;
+        if (lda < (M > 1 ? M : 1) || ldb < (K > 1 ? K : 1) || ldd < (M > 1 ? M : 1))
+            return TRSM_STATUS_INVALID_VALUE;
+        if (a_lower && M != K) return TRSM_STATUS_INVALID_VALUE;
+        if (split < 0 || split > M) return TRSM_STATUS_INVALID_VALUE;
+        if (D2 != nullptr && ldd2 < (split > 1 ? split : 1)) return TRSM_STATUS_INVALID_VALUE;
+        const Scalar b = read_alpha(dtype, beta);
+        const Scalar g = read_alpha(dtype, gamma);
+        const bool has_c = b.re != 0.0 || b.im != 0.0;
+        if (has_c && (C == nullptr || ldc < (M > 1 ? M : 1))) return TRSM_STATUS_INVALID_VALUE;
+        if (M == 0 || N == 0) return TRSM_STATUS_SUCCESS;
+        if (D == nullptr || (K > 0 && (A == nullptr || Bm == nullptr))) return TRSM_STATUS_INVALID_VALUE;
+        int dev = 0;
+        trsm_status_t s = check_device(&dev);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        GemmDesc gd{};
+        gd.M = M;
+        gd.N = N;
+        gd.K = K;
+        gd.A = A;
+        gd.lda = lda;
+        gd.Bm = Bm;
+        gd.ldb = ldb;
+        gd.C = has_c ? C : nullptr;
+        gd.ldc = has_c ? ldc : ldd;
+        gd.D = D;
+        gd.ldd = ldd;
+        gd.D2 = D2;
+        gd.ldd2 = ldd2;
+        gd.split = D2 ? split : 0;
+        gd.beta = b;
+        gd.gamma = g;
+        gd.a_lower = a_lower ? 1 : 0;
+        LaunchTimer t(a_lower ? TRSM_KERNEL_SOLVE_GEMM : TRSM_KERNEL_UPDATE_GEMM, dtype, M, N, K, 1,
+                      stream);
+        return hip_status(gemm_launch(dtype, gd, stream));
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
+trsm_status_t trsm_profile_start(void) {
+    try {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        for (ProfRec &r : g_prof) {
+            (void)hipEventSynchronize(r.stop);
+            g_event_pool.push_back(r.start);
+            g_event_pool.push_back(r.stop);
+        }
+        g_prof.clear();
+        g_prof_on = true;
+        return TRSM_STATUS_SUCCESS;
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
+trsm_status_t trsm_profile_stop(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = false;
+    return TRSM_STATUS_SUCCESS;
+}
+
+int64_t trsm_profile_count(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    return (int64_t)g_prof.size();
+}
+
+trsm_status_t trsm_profile_read(int64_t i, trsm_profile_record_t *rec) {
+    try {
+        if (rec == nullptr) return TRSM_STATUS_INVALID_VALUE;
+        ProfRec r;
+        {
+            std::lock_guard<std::mutex> lk(g_prof_mu);
+            if (i < 0 || i >= (int64_t)g_prof.size()) return TRSM_STATUS_INVALID_VALUE;
+            r = g_prof[(size_t)i];
+        }
+        if (hipEventSynchronize(r.stop) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+        *rec = r.r;
+        rec->ms = ms;
+        return TRSM_STATUS_SUCCESS;
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
+int trsm_lln_select_ib(trsm_dtype_t dtype, int64_t m, int64_t n) {
+    if (!valid_dtype(dtype) || m < 0 || n < 0) return 0;
+    return select_ib(dtype, m);
+}
+
+const char *trsm_status_string(trsm_status_t status) {
+    switch (status) {
+        case TRSM_STATUS_SUCCESS: return "success";
+        case TRSM_STATUS_INVALID_VALUE: return "invalid value";
+        case TRSM_STATUS_ALLOC_FAILED: return "workspace allocation failed";
+        case TRSM_STATUS_HIP_ERROR: return "HIP runtime error";
+        case TRSM_STATUS_NOT_SUPPORTED: return "not supported";
+        default: return "unknown status";
+    }
+}
+
+trsm_status_t trsm_release_workspace(void) {
+    try {
+        std::lock_guard<std::mutex> lk(g_mu);
+        trsm_status_t s = TRSM_STATUS_SUCCESS;
+        int cur = 0;
+        const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+        for (auto &kv : g_ws) {
+            if (!kv.second.first) continue;
+            if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+                s = TRSM_STATUS_HIP_ERROR;
+            (void)hipFree(kv.second.first);
+        }
+        g_ws.clear();
+        if (have_cur) (void)hipSetDevice(cur);
+        return s;
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
+}  // extern "C"

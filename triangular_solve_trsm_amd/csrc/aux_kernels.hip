@@ -1,0 +1,85 @@
+// Small memory kernels around the solve: zeroing B (alpha == 0, where the
+// result is X = 0 and A is not read) and copying one panel of B into the
+// panel buffer that the first diagonal-block solve reads.
+#include "scalar_ops.h"
+
+namespace trsm {
+namespace {
+
+template <typename T>
+__global__ __launch_bounds__(256) void fill_zero_kernel(int64_t m, int64_t n, T *__restrict__ B,
+                                                        int64_t ldb, int64_t strideB,
+                                                        int64_t batch) {
+    const int64_t total = m * n * batch;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = e % m;
+        const int64_t rest = e / m;
+        const int64_t j = rest % n;
+        const int64_t p = rest / n;
+        B[p * strideB + i + j * ldb] = Elem<T>::zero();
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void copy_panel_kernel(int64_t rows, int64_t n,
+                                                         const T *__restrict__ src, int64_t lds,
+                                                         T *__restrict__ dst, int64_t ldd) {
+    const int64_t total = rows * n;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = e % rows;
+        const int64_t j = e / rows;
+        dst[i + j * ldd] = src[i + j * lds];
+    }
+}
+
+inline unsigned grid_for(int64_t total) {
+    int64_t g = (total + 255) / 256;
+    if (g > 65536) g = 65536;  // grid-stride loops cover the rest
+    return (unsigned)(g < 1 ? 1 : g);
+}
+
+template <typename T>
+hipError_t fill_t(int64_t m, int64_t n, void *B, int64_t ldb, int64_t sB, int64_t batch,
+                  hipStream_t st) {
+    const int64_t total = m * n * batch;
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL((fill_zero_kernel<T>), dim3(grid_for(total)), dim3(256), 0, st, m, n,
+                       static_cast<T *>(B), ldb, sB, batch);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t copy_t(int64_t rows, int64_t n, const void *src, int64_t lds, void *dst, int64_t ldd,
+                  hipStream_t st) {
+    const int64_t total = rows * n;
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL((copy_panel_kernel<T>), dim3(grid_for(total)), dim3(256), 0, st, rows, n,
+                       static_cast<const T *>(src), lds, static_cast<T *>(dst), ldd);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t fill_zero_launch(int dtype, int64_t m, int64_t n, void *B, int64_t ldb,
+                            int64_t strideB, int64_t batch, hipStream_t stream) {
+    switch (dtype) {
+        case R32F: return fill_t<float>(m, n, B, ldb, strideB, batch, stream);
+        case R64F: return fill_t<double>(m, n, B, ldb, strideB, batch, stream);
+        case C64F: return fill_t<cplx>(m, n, B, ldb, strideB, batch, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t copy_panel_launch(int dtype, int64_t rows, int64_t n, const void *src, int64_t lds,
+                             void *dst, int64_t ldd, hipStream_t stream) {
+    switch (dtype) {
+        case R32F: return copy_t<float>(rows, n, src, lds, dst, ldd, stream);
+        case R64F: return copy_t<double>(rows, n, src, lds, dst, ldd, stream);
+        case C64F: return copy_t<cplx>(rows, n, src, lds, dst, ldd, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace trsm

@@ -1,0 +1,74 @@
+// Internal interfaces between the host dispatcher (api.cpp) and the gfx950
+// kernels (small_lln.hip, diag_inv.hip, gemm_mfma.hip, aux_kernels.hip).
+// Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace trsm {
+
+// Element types.  `cplx` is an interleaved (re, im) pair of doubles,
+// layout-compatible with hipDoubleComplex.
+struct alignas(16) cplx {
+    double re, im;
+};
+
+enum DType : int { R32F = 0, R64F = 1, C64F = 2 };
+
+inline size_t dtype_size(int dt) {
+    return dt == R32F ? 4 : dt == R64F ? 8 : 16;
+}
+
+// Scalars travel between host and device code as a pair of doubles
+// (fp32 values are widened; only `re` is used for real types).
+struct Scalar {
+    double re, im;
+};
+
+// ---- kernel (a): single-workgroup direct solve, m <= 64 ------------------
+// One workgroup per (problem, group of 64 right-hand-side columns).
+hipError_t small_lln_launch(int dtype, int m, int64_t n, Scalar alpha, const void *A,
+                            int64_t lda, int64_t strideA, void *B, int64_t ldb,
+                            int64_t strideB, int64_t batch, hipStream_t stream);
+
+// ---- kernel (b1): inversion of every ib x ib diagonal block ---------------
+// W receives ceil(m/ib) blocks, block t at W + t*ib*ib (column-major, ld ib),
+// each lower triangular with explicit zeros above the diagonal.
+hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t lda,
+                           void *W, hipStream_t stream);
+
+// ---- kernels (b2, b3): MFMA GEMM -----------------------------------------
+//   D = beta * C + gamma * (A * Bm)
+// A: M x K (lda), Bm: K x N (ldb), C/D: M x N, all column-major.
+// Output rows [0, split) go to D2 (ldd2) instead of D (ldd); split % 16 == 0.
+// C may alias D (in place).  beta == 0 means C is not read (may be null).
+// a_lower != 0: A is lower triangular (explicit zeros above the diagonal);
+// K-tiles to the right of a row tile's diagonal are skipped (requires M == K).
+struct GemmDesc {
+    int64_t M, N, K;
+    const void *A;
+    int64_t lda;
+    const void *Bm;
+    int64_t ldb;
+    const void *C;
+    int64_t ldc;
+    void *D;
+    int64_t ldd;
+    void *D2;
+    int64_t ldd2;
+    int64_t split;
+    Scalar beta, gamma;
+    int a_lower;
+};
+hipError_t gemm_launch(int dtype, const GemmDesc &g, hipStream_t stream);
+
+// ---- auxiliary kernels ----------------------------------------------------
+// B[p] <- 0 for an m x n column-major matrix per problem.
+hipError_t fill_zero_launch(int dtype, int64_t m, int64_t n, void *B, int64_t ldb,
+                            int64_t strideB, int64_t batch, hipStream_t stream);
+// dst (rows x n, ldd) <- src (rows x n, lds).
+hipError_t copy_panel_launch(int dtype, int64_t rows, int64_t n, const void *src,
+                             int64_t lds, void *dst, int64_t ldd, hipStream_t stream);
+
+}  // namespace trsm
