@@ -16,7 +16,7 @@ one).  Batched operands are (batch, m, n) with strides (stride, 1, ld).
 Supported dtypes: torch.float32, torch.float64, torch.complex128.  B is
 overwritten with X such that L X = alpha B, L the lower triangle of A.
 
-The library must have been built (``python -m triangular_solve_trsm_amd.build``
+The library must have been built (``python triangular_solve_trsm_amd/build.py``
 or ``__graft_entry__.build()``); importing this package without it raises.
 """
 from __future__ import annotations
@@ -55,7 +55,7 @@ class TrsmError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m triangular_solve_trsm_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python triangular_solve_trsm_amd/build.py` "
             "(there is no fallback implementation)")
     lib = ctypes.CDLL(LIB_PATH)
     i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
