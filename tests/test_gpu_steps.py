@@ -1,0 +1,146 @@
+"""GPU checks of the step-level entry points (include/trsm_kernels.h).
+
+* trsm_kernel_gemm (the phase-2 GEMM of the blocked algorithm) against a
+  float64 / complex128 numpy product, element by element, within the
+  standard rounding bound of a K-term dot product:
+      |D - D_ref| <= 2 (K + 2) u (|beta| |C| + |gamma| |A| |Bm|)   (per element)
+  on ragged shapes, odd leading dimensions, the split routing to D2, the
+  triangular skip, both macro-tile sizes, K = 0 and gamma = 0.
+* trsm_kernel_diag_inv (phase 1) against the oracle solving each diagonal
+  block against the columns of the identity, which is the definition of the
+  inverse the pages build the kernel on (section 4.3.1, the identity tile
+  E_j as right-hand side).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import NP, from_dev, to_dev
+from trsm_inputs import make_problem
+
+pytestmark = pytest.mark.gpu
+
+U = {"f32": 2.0 ** -24, "f64": 2.0 ** -53, "c64": 2.0 ** -53}
+
+
+@pytest.fixture(scope="module")
+def T():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import triangular_solve_trsm_amd as T
+    return T
+
+
+def rand(dtype, rows, cols, rng, ld=None):
+    if dtype == "c64":
+        a = rng.uniform(-1, 1, (rows, cols)) + 1j * rng.uniform(-1, 1, (rows, cols))
+    else:
+        a = rng.uniform(-1, 1, (rows, cols))
+    a = a.astype(NP[dtype])
+    ld = rows if ld is None else ld
+    base = np.full((cols, max(ld, 1)), np.nan, dtype=NP[dtype])
+    base.T[:rows] = a
+    return base.T[:rows]
+
+
+def gemm_case(T, dtype, M, N, K, beta, gamma, *, seed=0, ldpad=0, split=0, a_lower=False):
+    import torch
+    rng = np.random.default_rng(seed)
+    A = rand(dtype, M, K, rng, M + ldpad)
+    if a_lower:
+        A = np.asfortranarray(np.tril(A))
+        A = rand_like_ld(A, M + ldpad)
+    Bm = rand(dtype, K, N, rng, K + ldpad)
+    C = rand(dtype, M, N, rng, M + ldpad)
+    Ad, Bd, Cd = to_dev(A), to_dev(Bm), to_dev(C)
+    Dd = to_dev(np.full((M, N), np.nan, dtype=NP[dtype], order="F"), ld=M + ldpad)
+    D2d = to_dev(np.full((max(split, 1), N), np.nan, dtype=NP[dtype], order="F")) if split else None
+    T.trsm_kernel_gemm(Ad, Bd, Dd, beta=beta, gamma=gamma, C=Cd if beta != 0 else None,
+                       D2=D2d, split=split, a_lower=a_lower)
+    torch.cuda.synchronize()
+    D = from_dev(Dd)
+    if split:
+        D = D.copy()
+        D[:split] = from_dev(D2d)[:split]
+    wide = np.complex128 if dtype == "c64" else np.float64
+    A64, B64, C64 = A.astype(wide), Bm.astype(wide), C.astype(wide)
+    ref = gamma * (A64 @ B64) + (beta * C64 if beta != 0 else 0)
+    scale = abs(gamma) * (np.abs(A64) @ np.abs(B64)) + (abs(beta) * np.abs(C64) if beta != 0 else 0)
+    bound = 2 * (K + 2) * U[dtype] * scale + 1e-300
+    err = np.abs(D.astype(wide) - ref)
+    assert np.all(np.isfinite(D)), f"non-finite output {dtype} {M}x{N}x{K}"
+    worst = float(np.max(err / bound)) if err.size else 0.0
+    assert worst <= 1.0, f"{dtype} M={M} N={N} K={K}: error {worst:.2f} x the rounding bound"
+    return worst
+
+
+def rand_like_ld(a, ld):
+    rows, cols = a.shape
+    base = np.full((cols, max(ld, 1)), np.nan, dtype=a.dtype)
+    base.T[:rows] = a
+    return base.T[:rows]
+
+
+SHAPES = [(1, 1, 1), (17, 33, 5), (130, 129, 37), (64, 64, 64), (200, 70, 257), (513, 300, 48)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+def test_gemm_ragged_shapes(T, dtype):
+    for i, (M, N, K) in enumerate(SHAPES):
+        for beta, gamma in [(0.0, 1.0), (1.0, -1.0), (0.5, -1.0), (-2.0, 0.75)]:
+            if dtype == "c64":
+                beta, gamma = complex(beta, 0.25 if beta else 0.0), complex(gamma, -0.5)
+            gemm_case(T, dtype, M, N, K, beta, gamma, seed=i)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+def test_gemm_large_tile_path(T, dtype):
+    """Enough 128 x 128 tiles (>= 512) to take the large macro tile, with a
+    ragged K tile and odd leading dimensions (unaligned 16-byte loads)."""
+    M = 1450 if dtype == "c64" else 2900
+    gemm_case(T, dtype, M, 2900, 45, 1.0, -1.0, seed=3)
+    gemm_case(T, dtype, M, 2900, 40, 0.0, 1.0, seed=4, ldpad=3)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+def test_gemm_split_routing(T, dtype):
+    for split in (16, 37, 100):
+        gemm_case(T, dtype, 300, 90, 64, 1.0, -1.0, seed=split, split=split)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+def test_gemm_triangular(T, dtype):
+    for M in (64, 100, 256, 300):
+        gemm_case(T, dtype, M, 150, M, 0.0, 0.5, seed=M, a_lower=True)
+
+
+@pytest.mark.parametrize("dtype", ["f64", "c64"])
+def test_gemm_k_zero_and_gamma_zero(T, dtype):
+    gemm_case(T, dtype, 50, 40, 0, 1.5, -1.0, seed=1)
+    gemm_case(T, dtype, 50, 40, 30, 1.5, 0.0, seed=2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("ib", [64, 128, 256, 512])
+def test_diag_inv_vs_oracle_identity_solve(T, dtype, ib):
+    import torch
+    m = ib * 2 + 37  # two full blocks and a ragged one
+    L, _ = make_problem(dtype, m, 1, seed=ib)
+    nb = (m + ib - 1) // ib
+    W = torch.full((nb * ib * ib,), float("nan"), dtype={"f32": torch.float32, "f64": torch.float64,
+                                                         "c64": torch.complex128}[dtype], device="cuda")
+    T.trsm_kernel_diag_inv(to_dev(L), W, ib)
+    torch.cuda.synchronize()
+    Wh = from_dev(W)
+    tol = 1e-5 if dtype == "f32" else 1e-13
+    for t in range(nb):
+        r0 = t * ib
+        bs = min(ib, m - r0)
+        D = np.asfortranarray(L[r0:r0 + bs, r0:r0 + bs])
+        ref = oracle.solve(D, np.asfortranarray(np.eye(bs, dtype=D.dtype)), 1.0)
+        Wt = Wh[t * ib * ib:(t + 1) * ib * ib].reshape(ib, ib).T[:bs, :bs]
+        assert np.all(np.triu(Wt, 1) == 0), "upper triangle of the inverse must be explicit zeros"
+        e = np.linalg.norm(Wt - ref) / np.linalg.norm(ref)
+        assert e <= tol, (dtype, ib, t, e)

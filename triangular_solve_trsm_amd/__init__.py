@@ -119,6 +119,8 @@ def _stream_handle(stream) -> int:
 
 def _ld(t, rows: int, cols: int) -> int:
     """Leading dimension of a column-major 2-D view (stride(-2) must be 1)."""
+    if rows == 0 or cols == 0:
+        return max(rows, 1)  # empty operand: its strides mean nothing
     s0, s1 = t.stride(-2), t.stride(-1)
     if rows > 1 and s0 != 1:
         raise ValueError("operand must be column-major: stride of the row index must be 1")

@@ -14,18 +14,37 @@
 // skips the K-tiles right of each row tile's diagonal (the solve GEMM).
 //
 // gfx950 mapping:
-//   * 256 threads = 2 x 2 wavefronts, macro tile MT x NT (real rows x cols),
-//     each wave 64 x 64 built from 4 x 4 tiles of v_mfma_f64_16x16x4f64 (fp64,
-//     complex) or v_mfma_f32_16x16x4f32 (fp32, true fp32 products);
-//   * operands are staged in LDS, double-buffered: the global loads of K-tile
-//     t+1 are in flight while the MFMAs of tile t run, one barrier per tile;
+//   * 256 threads = 2 x 2 wavefronts on a macro tile of MT x NT real rows x
+//     columns (128 x 128, or 64 x 64 when a launch has too few tiles to give
+//     every CU two of them); each wave owns (MT/2) x (NT/2) as 16 x 16 tiles
+//     of v_mfma_f64_16x16x4f64 (fp64, complex fp64) or
+//     v_mfma_f32_16x16x4f32 (fp32: true fp32 products, no reduced-precision
+//     splitting);
+//   * global loads are raw buffer loads of 16 bytes per lane: reads past the
+//     end of an operand return zero without a branch, and a K tile that
+//     runs past K is zeroed by a select, so ragged shapes cost nothing in the
+//     main loop;
+//   * operands are staged through LDS, double-buffered: the loads of K tile
+//     t+1 are in flight while the MFMAs of tile t run, one barrier per tile.
+//     A is kept as [k][row] (its global layout), Bm as [column][k] (its
+//     global layout too), with pads that spread the fragment reads over all
+//     LDS banks;
+//   * inside a K tile lane group q (lane / 16) works on k = q*KT/4 ... so
+//     each lane's Bm fragments for consecutive MFMAs are adjacent in LDS and
+//     come in 16-byte reads (the order of a sum over k is free);
+//   * the rows fed to the A operand are permuted so that every lane ends
+//     with runs of consecutive output rows: C is read and D written in
+//     16-byte pieces;
+//   * C is read at the start of a tile, straight into the accumulators
+//     (acc = (beta/gamma) C, D = gamma acc), so its latency overlaps the
+//     first operand loads instead of stalling the end of the tile;
 //   * complex fp64 uses the real 2x2 embedding: a complex M x K by K x N
 //     product is a real (2M x 2K) by (2K x N) product where each complex
 //     a = ar + i ai of A becomes [[ar, -ai], [ai, ar]]; the interleaved
 //     storage of Bm is already its real (2K x N) view, the A fragment is
 //     expanded on the fly from the complex tile in LDS, and the real rows are
-//     ordered so that each lane ends up holding whole complex results.  This
-//     is exactly the 4 real products per complex product (no 3M trick);
+//     ordered so that each lane holds whole complex results.  This is exactly
+//     the 4 real products per complex product (no 3M trick);
 //   * tiles are mapped so that each XCD (8 per chip, each with its own L2)
 //     works on a band of 8 column tiles at a time, and the workgroups of one
 //     XCD cover roughly 8 x 8 tiles, sharing the A and Bm panels in its L2.
@@ -39,51 +58,71 @@ namespace {
 typedef double d4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef double d2v __attribute__((ext_vector_type(2)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource of a gfx9-family part (gfx950): base address, no
+// stride, a byte range (loads at or past it return 0), 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const uint32_t n =
+        bytes >= 0xffffffffLL ? 0xffffffffu : (bytes <= 0 ? 0u : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                             0x00020000);
+}
+
+// 16 bytes at byte offset `off`; `vec` says the address is 16-byte aligned,
+// otherwise four dword loads are used (every element type here is at least
+// dword aligned).
+__device__ __forceinline__ u4v ld16(__amdgpu_buffer_rsrc_t r, uint32_t off, int vec) {
+    if (vec) return __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    u4v v;
+    v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    v[1] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4, 0, 0);
+    v[2] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 8, 0, 0);
+    v[3] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 12, 0, 0);
+    return v;
+}
 
 template <typename T> struct GemmTraits;
 template <> struct GemmTraits<float> {
     using R = float;
     using Acc = f4;
-    using Vec = f4;  // 16-byte global load unit
-    static constexpr int kVec = 4;
     static constexpr bool kCplx = false;
     __device__ __forceinline__ static Acc mfma(R a, R b, Acc c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
-    // Row of the 16x16 result held by item v of a lane in group q = lane/16.
-    __device__ __forceinline__ static int out_row(int q, int v) { return 4 * q + v; }
+    // Row of a 16-row block fed by lane c of the A operand.  The f32 result
+    // puts rows 4q .. 4q+3 in lane group q already.
+    __device__ __forceinline__ static int a_row(int c) { return c; }
 };
 template <> struct GemmTraits<double> {
     using R = double;
     using Acc = d4;
-    using Vec = d2v;
-    static constexpr int kVec = 2;
     static constexpr bool kCplx = false;
     __device__ __forceinline__ static Acc mfma(R a, R b, Acc c) {
         return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
     }
-    // The f64 variant interleaves the other way (checked on gfx950).
-    __device__ __forceinline__ static int out_row(int q, int v) { return q + 4 * v; }
+    // The f64 result holds MFMA row q + 4v in item v of lane group q
+    // (checked on gfx950); feeding row 4(c%4) + c/4 as MFMA row c turns that
+    // into rows 4q .. 4q+3.
+    __device__ __forceinline__ static int a_row(int c) { return 4 * (c & 3) + (c >> 2); }
 };
 template <> struct GemmTraits<cplx> {
     using R = double;
     using Acc = d4;
-    using Vec = d2v;
-    static constexpr int kVec = 2;
     static constexpr bool kCplx = true;
     __device__ __forceinline__ static Acc mfma(R a, R b, Acc c) {
         return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
     }
-    __device__ __forceinline__ static int out_row(int q, int v) { return q + 4 * v; }
+    __device__ __forceinline__ static int a_row(int c) { return c; }
 };
 
 template <typename T>
 struct GemmParams {
     int64_t M, N, K;  // in elements of T (complex counts for cplx)
     const T *A;
-    int64_t lda;
+    int64_t lda, extA;  // extA: elements from A to one past the last one used
     const T *Bm;
-    int64_t ldb;
+    int64_t ldb, extB;
     const T *C;
     int64_t ldc;
     T *D;
@@ -91,10 +130,10 @@ struct GemmParams {
     T *D2;
     int64_t ldd2;
     int64_t split;
-    Scalar beta, gamma;
+    Scalar sc, gamma;  // accumulators start at sc * C; D = gamma * acc
     int has_c;
-    int a_vec;  // 16-byte vector loads of A columns are aligned
-    int b_vec;  // same for Bm
+    int a_vec, b_vec;        // 16-byte aligned operand loads
+    int c_vec, d_vec, d2_vec;  // 16-byte aligned C / D / D2 columns
     int tilesM, tilesN;
 };
 
@@ -116,6 +155,47 @@ __device__ __forceinline__ void map_tile(int w, int tilesM, int tilesN, int &tm,
     tn = band * 8 + (r - (r / wb) * wb);
 }
 
+// ---- C / D access in the accumulator layout -------------------------------
+// Real types: a lane holds rows r .. r+3 (r % 4 == 0) of column j in items
+// 0..3 of an accumulator.
+
+template <typename R>
+__device__ __forceinline__ void load_rows4(const R *X, int64_t ld, int64_t M, int64_t r, int64_t j,
+                                           int vec, R out[4]) {
+    const R *col = X + j * ld;
+    if (vec && r + 3 < M) {
+        if constexpr (sizeof(R) == 4) {
+            const f4 v = *reinterpret_cast<const f4 *>(col + r);
+            out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+        } else {
+            const d2v v0 = *reinterpret_cast<const d2v *>(col + r);
+            const d2v v1 = *reinterpret_cast<const d2v *>(col + r + 2);
+            out[0] = v0[0]; out[1] = v0[1]; out[2] = v1[0]; out[3] = v1[1];
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) out[v] = (r + v < M) ? col[r + v] : R(0);
+    }
+}
+
+template <typename R>
+__device__ __forceinline__ void store_rows4(R *X, int64_t ld, int64_t lim, int64_t r, int64_t j,
+                                            int vec, const R in[4]) {
+    R *col = X + j * ld;
+    if (vec && r + 3 < lim) {
+        if constexpr (sizeof(R) == 4) {
+            *reinterpret_cast<f4 *>(col + r) = f4{in[0], in[1], in[2], in[3]};
+        } else {
+            *reinterpret_cast<d2v *>(col + r) = d2v{in[0], in[1]};
+            *reinterpret_cast<d2v *>(col + r + 2) = d2v{in[2], in[3]};
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            if (r + v < lim) col[r + v] = in[v];
+    }
+}
+
 // TRI: A is lower triangular (the solve GEMM); a separate instantiation so
 // that the solve and the update appear as distinct kernels in traces.
 template <typename T, int MT, int NT, int KT, bool TRI>
@@ -123,34 +203,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     using Tr = GemmTraits<T>;
     using R = typename Tr::R;
     using Acc = typename Tr::Acc;
-    using Vec = typename Tr::Vec;
     constexpr bool CPLX = Tr::kCplx;
-    constexpr int VEC = Tr::kVec;
-    constexpr int WM = MT / 2, WN = NT / 2;  // per-wave tile
+    constexpr int VR = 16 / (int)sizeof(R);  // reals per 16-byte load
+    constexpr int WM = MT / 2, WN = NT / 2;  // per-wave tile (real rows x cols)
     constexpr int FM = WM / 16, FN = WN / 16;
-    // LDS: A as [k][row] (rows contiguous), Bm as [k][col] (cols contiguous).
-    constexpr int PADA = CPLX ? 1 : VEC;  // keeps 16-byte alignment of A rows
-    constexpr int PADB = 1;
-    constexpr int AROWS = CPLX ? MT / 2 : MT;  // complex rows for cplx
+    constexpr int KS = KT / 4;  // k values of one lane group inside a K tile
+    constexpr int CW = VR;      // k values per 16-byte Bm fragment read
+    static_assert(KS % CW == 0, "K tile");
+    // A tile: AK columns x AR rows of T (complex: complex rows and k).
     constexpr int AK = CPLX ? KT / 2 : KT;
-    using AS = typename std::conditional<CPLX, cplx, R>::type;
-    __shared__ AS As[2][AK][AROWS + PADA];
-    __shared__ R Bs[2][KT][NT + PADB];
+    constexpr int AR = CPLX ? MT / 2 : MT;
+    constexpr int AU = CPLX ? 1 : VR;  // elements of T per 16-byte load
+    constexpr int SA = AR + 4;         // row pitch: lane groups land 32 banks apart
+    constexpr int SB = KT + (VR == 4 ? 4 : 2);  // 36 (f32) / 18 (f64) reals: 9 x 16 bytes
+    __shared__ __attribute__((aligned(16))) T As[2][AK][SA];
+    __shared__ __attribute__((aligned(16))) R Bs[2][NT][SB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
+    const int c16 = lane & 15;
+    const int q = lane >> 4;
 
-    int tm, tn;
     if (blockIdx.x >= (unsigned)(p.tilesM * p.tilesN)) return;
+    int tm, tn;
     map_tile(blockIdx.x, p.tilesM, p.tilesN, tm, tn);
 
-    // Real-view sizes: complex rows and K count twice.
-    const int64_t Mr = CPLX ? 2 * p.M : p.M;
-    const int64_t Kr = CPLX ? 2 * p.K : p.K;
-    const int64_t i0 = (int64_t)tm * MT;  // real row offset of the tile
+    const int64_t Kr = CPLX ? 2 * p.K : p.K;  // real K
+    const int64_t i0 = (int64_t)tm * MT;      // real row offset of the tile
     const int64_t j0 = (int64_t)tn * NT;
+    const int64_t i0t = CPLX ? i0 / 2 : i0;
     int64_t kend = Kr;
     if (TRI) {
         const int64_t lim = i0 + MT;  // real rows; K has the same (real) scale
@@ -158,112 +241,122 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     }
     const int nkt = (int)((kend + KT - 1) / KT);
 
-    const R *Ar = reinterpret_cast<const R *>(p.A);
-    const R *Br = reinterpret_cast<const R *>(p.Bm);
-    const int64_t ldbr = CPLX ? 2 * p.ldb : p.ldb;
+    // ---- accumulators start at sc * C ----------------------------------
+    Acc acc[FM][FN];
+    if (p.has_c) {
+        if constexpr (CPLX) {
+            const cplx sc{p.sc.re, p.sc.im};
+#pragma unroll
+            for (int a = 0; a < FM; ++a) {
+                const int64_t cb = (i0 + wm * WM + a * 16) / 2 + 2 * q;  // complex rows cb, cb+1
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const int64_t j = j0 + wn * WN + b * 16 + c16;
+                    cplx z0{0.0, 0.0}, z1{0.0, 0.0};
+                    if (j < p.N) {
+                        if (cb < p.M) z0 = Elem<cplx>::mul(sc, p.C[cb + j * p.ldc]);
+                        if (cb + 1 < p.M) z1 = Elem<cplx>::mul(sc, p.C[cb + 1 + j * p.ldc]);
+                    }
+                    acc[a][b] = Acc{z0.re, z0.im, z1.re, z1.im};
+                }
+            }
+        } else {
+            const R sc = (R)p.sc.re;
+#pragma unroll
+            for (int a = 0; a < FM; ++a) {
+                const int64_t r = i0 + wm * WM + a * 16 + 4 * q;
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const int64_t j = j0 + wn * WN + b * 16 + c16;
+                    R cv[4] = {R(0), R(0), R(0), R(0)};
+                    if (j < p.N) load_rows4<R>(p.C, p.ldc, p.M, r, j, p.c_vec, cv);
+                    acc[a][b] = Acc{sc * cv[0], sc * cv[1], sc * cv[2], sc * cv[3]};
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int a = 0; a < FM; ++a)
+#pragma unroll
+            for (int b = 0; b < FN; ++b) acc[a][b] = Acc{0, 0, 0, 0};
+    }
 
     // ---- global -> register staging ------------------------------------
-    // A real: MT rows x KT cols, VEC rows per thread-load.
-    constexpr int A_TPC = CPLX ? AROWS : MT / VEC;   // threads per column
-    constexpr int A_CPP = 256 / A_TPC;               // columns per pass
+    constexpr int A_TPC = AR / AU;  // threads per A column
+    constexpr int A_CPP = 256 / A_TPC;
     constexpr int A_PASSES = AK / A_CPP;
     static_assert(A_PASSES * A_CPP == AK, "A tile shape");
-    // Bm: KT (real) rows x NT cols, VEC rows per thread-load.
-    constexpr int B_TPC = KT / VEC;
+    constexpr int B_TPC = KT / VR;  // threads per Bm column (real view)
     constexpr int B_CPP = 256 / B_TPC;
     constexpr int B_PASSES = NT / B_CPP;
     static_assert(B_PASSES * B_CPP == NT, "B tile shape");
+    constexpr int DW = (int)sizeof(R) / 4;  // dwords per real
 
-    Vec ra[A_PASSES];
-    Vec rb[B_PASSES];
+    u4v ra[A_PASSES];
+    u4v rb[B_PASSES];
 
     auto load_tiles = [&](int kt) {
         const int64_t k0 = (int64_t)kt * KT;  // real k offset
+        const int64_t k0t = CPLX ? k0 / 2 : k0;
+        {
+            const int64_t off = i0t + k0t * p.lda;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.A + off, (p.extA - off) * (int64_t)sizeof(T));
 #pragma unroll
-        for (int q = 0; q < A_PASSES; ++q) {
-            const int flat = q * 256 + tid;
-            const int kk = flat / A_TPC;
-            const int rr = flat - kk * A_TPC;
-            Vec v;
-            if constexpr (CPLX) {
-                const int64_t ic = i0 / 2 + rr;
-                const int64_t kc = k0 / 2 + kk;
-                v = Vec{0.0, 0.0};
-                if (ic < p.M && kc < p.K) v = *reinterpret_cast<const Vec *>(Ar + 2 * (ic + kc * p.lda));
-            } else {
-                const int64_t i = i0 + (int64_t)rr * VEC;
-                const int64_t k = k0 + kk;
-                if (k < Kr && i + VEC <= Mr && p.a_vec) {
-                    v = *reinterpret_cast<const Vec *>(Ar + i + k * p.lda);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        v[e] = (k < Kr && i + e < Mr) ? Ar[i + e + k * p.lda] : R(0);
-                }
+            for (int s = 0; s < A_PASSES; ++s) {
+                const int flat = s * 256 + tid;
+                const int kk = flat / A_TPC;
+                const int rr = flat - kk * A_TPC;
+                const uint32_t boff = (uint32_t)(((int64_t)rr * AU + (int64_t)kk * p.lda) * (int64_t)sizeof(T));
+                u4v v = ld16(rs, boff, p.a_vec);
+                if (k0t + kk >= p.K) v = u4v{0u, 0u, 0u, 0u};
+                ra[s] = v;
             }
-            ra[q] = v;
         }
+        {
+            const int64_t off = k0t + j0 * p.ldb;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.Bm + off, (p.extB - off) * (int64_t)sizeof(T));
 #pragma unroll
-        for (int q = 0; q < B_PASSES; ++q) {
-            const int flat = q * 256 + tid;
-            const int jj = flat / B_TPC;
-            const int kv = (flat - jj * B_TPC) * VEC;
-            const int64_t j = j0 + jj;
-            const int64_t k = k0 + kv;
-            Vec v;
-            if (j < p.N && k + VEC <= Kr && p.b_vec) {
-                v = *reinterpret_cast<const Vec *>(Br + k + j * ldbr);
-            } else {
+            for (int s = 0; s < B_PASSES; ++s) {
+                const int flat = s * 256 + tid;
+                const int jj = flat / B_TPC;
+                const int kv = (flat - jj * B_TPC) * VR;  // real k inside the tile
+                const int64_t kvt = CPLX ? kv / 2 : kv;
+                const uint32_t boff = (uint32_t)((kvt + (int64_t)jj * p.ldb) * (int64_t)sizeof(T));
+                u4v v = ld16(rs, boff, p.b_vec);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    v[e] = (j < p.N && k + e < Kr) ? Br[k + e + j * ldbr] : R(0);
+                for (int e = 0; e < VR; ++e)
+                    if (k0 + kv + e >= Kr)
+#pragma unroll
+                        for (int d = 0; d < DW; ++d) v[e * DW + d] = 0u;
+                rb[s] = v;
             }
-            rb[q] = v;
         }
     };
 
     auto store_tiles = [&](int buf) {
 #pragma unroll
-        for (int q = 0; q < A_PASSES; ++q) {
-            const int flat = q * 256 + tid;
+        for (int s = 0; s < A_PASSES; ++s) {
+            const int flat = s * 256 + tid;
             const int kk = flat / A_TPC;
             const int rr = flat - kk * A_TPC;
-            if constexpr (CPLX) {
-                As[buf][kk][rr] = cplx{ra[q][0], ra[q][1]};
-            } else {
-                *reinterpret_cast<Vec *>(&As[buf][kk][rr * VEC]) = ra[q];
-            }
+            *reinterpret_cast<u4v *>(&As[buf][kk][rr * AU]) = ra[s];
         }
 #pragma unroll
-        for (int q = 0; q < B_PASSES; ++q) {
-            const int flat = q * 256 + tid;
+        for (int s = 0; s < B_PASSES; ++s) {
+            const int flat = s * 256 + tid;
             const int jj = flat / B_TPC;
-            const int kv = (flat - jj * B_TPC) * VEC;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) Bs[buf][kv + e][jj] = rb[q][e];
+            const int kv = (flat - jj * B_TPC) * VR;
+            *reinterpret_cast<u4v *>(&Bs[buf][jj][kv]) = rb[s];
         }
     };
 
-    Acc acc[FM][FN];
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
-#pragma unroll
-        for (int b = 0; b < FN; ++b) acc[a][b] = Acc{0, 0, 0, 0};
-
-    // Complex A-fragment expansion constants (lane-fixed).
-    // Real k' = 2*kc + ki follows the interleaved storage of Bm.  Real rows
-    // are ordered so that the f64 MFMA result (row q + 4v in lane group q,
-    // item v) holds the real and imaginary part of one complex row in items
-    // (0, 1) and of another in items (2, 3): inside a 16-row MFMA tile, real
-    // row t stands for complex row (t % 4) + 4 * (t / 8), part (t / 4) % 2.
-    // Entry (row, k') of the embedded A is re if the parts agree, im for
-    // (im row, re col) and -im for (re row, im col).
-    const int t16 = lane & 15;
-    const int a_crow = (t16 & 3) + 4 * (t16 >> 3);
-    const int ri = (t16 >> 2) & 1;
-    const int ki = (lane >> 4) & 1;
-    const int a_part = (ri != ki) ? 1 : 0;
-    const R a_sign = (ri == 0 && ki == 1) ? R(-1) : R(1);
+    // Complex A-fragment expansion (lane-fixed part).  Real row t = c16 of a
+    // 16-row block stands for complex row 2(t % 4) + t / 8 of the block's 8,
+    // part (t / 4) % 2; with the f64 result layout (row q + 4v in item v) a
+    // lane then holds complex rows 2q (items 0, 1) and 2q + 1 (items 2, 3).
+    const int a_crow = 2 * (c16 & 3) + (c16 >> 3);
+    const int a_ri = (c16 >> 2) & 1;
+    const int a_row = Tr::a_row(c16);
 
     if (nkt > 0) {
         load_tiles(0);
@@ -273,25 +366,41 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
             const int buf = kt & 1;
             if (kt + 1 < nkt) load_tiles(kt + 1);
 #pragma unroll
-            for (int ks = 0; ks < KT; ks += 4) {
-                const int kr = ks + (lane >> 4);  // real k within the tile
-                R af[FM], bf[FN];
+            for (int s0 = 0; s0 < KS; s0 += CW) {
+                const int kb = q * KS + s0;  // real k of this chunk inside the tile
+                R bf[FN][CW];
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const u4v v = *reinterpret_cast<const u4v *>(&Bs[buf][wn * WN + b * 16 + c16][kb]);
+                    if constexpr (sizeof(R) == 4) {
+                        const f4 fv = __builtin_bit_cast(f4, v);
+#pragma unroll
+                        for (int e = 0; e < CW; ++e) bf[b][e] = fv[e];
+                    } else {
+                        const d2v dv = __builtin_bit_cast(d2v, v);
+                        bf[b][0] = dv[0];
+                        bf[b][1] = dv[1];
+                    }
+                }
+                R af[FM][CW];
 #pragma unroll
                 for (int a = 0; a < FM; ++a) {
                     if constexpr (CPLX) {
-                        const int crow = (wm * WM + a * 16) / 2 + a_crow;  // complex row in tile
-                        const cplx &z = As[buf][kr >> 1][crow];
-                        af[a] = (a_part ? z.im : z.re) * a_sign;
+                        // real k = kb + e: complex k (kb + e) / 2, part e % 2 (kb even)
+                        const cplx z = As[buf][kb >> 1][(wm * WM + a * 16) / 2 + a_crow];
+                        af[a][0] = a_ri ? z.im : z.re;    // k part 0
+                        af[a][1] = a_ri ? z.re : -z.im;   // k part 1
                     } else {
-                        af[a] = As[buf][kr][wm * WM + a * 16 + (lane & 15)];
+#pragma unroll
+                        for (int e = 0; e < CW; ++e) af[a][e] = As[buf][kb + e][wm * WM + a * 16 + a_row];
                     }
                 }
 #pragma unroll
-                for (int b = 0; b < FN; ++b) bf[b] = Bs[buf][kr][wn * WN + b * 16 + (lane & 15)];
+                for (int e = 0; e < CW; ++e)
 #pragma unroll
-                for (int a = 0; a < FM; ++a)
+                    for (int a = 0; a < FM; ++a)
 #pragma unroll
-                    for (int b = 0; b < FN; ++b) acc[a][b] = Tr::mfma(af[a], bf[b], acc[a][b]);
+                        for (int b = 0; b < FN; ++b) acc[a][b] = Tr::mfma(af[a][e], bf[b][e], acc[a][b]);
             }
             if (kt + 1 < nkt) {
                 store_tiles(buf ^ 1);
@@ -300,64 +409,64 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         }
     }
 
-    // ---- epilogue: D = beta*C + gamma*acc ------------------------------
-    // Item v of a lane in group q = lane/16 holds row Tr::out_row(q, v),
-    // column lane % 16, of each 16 x 16 sub-tile.
-    const int q = lane >> 4;
-    const int cc = lane & 15;
+    // ---- epilogue: D = gamma * acc, rows below `split` to D2 --------------
     if constexpr (CPLX) {
-        const cplx beta{p.beta.re, p.beta.im};
         const cplx gamma{p.gamma.re, p.gamma.im};
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
+            const int64_t cb = (i0 + wm * WM + a * 16) / 2 + 2 * q;
 #pragma unroll
             for (int b = 0; b < FN; ++b) {
-                const int64_t j = j0 + wn * WN + b * 16 + cc;
+                const int64_t j = j0 + wn * WN + b * 16 + c16;
                 if (j >= p.N) continue;
-                const int64_t cbase = (i0 + wm * WM + a * 16) / 2;  // first complex row
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int64_t ic = cbase + q + 4 * h;
+                    const int64_t ic = cb + h;
                     if (ic >= p.M) continue;
-                    cplx z{acc[a][b][2 * h], acc[a][b][2 * h + 1]};
-                    cplx out = Elem<cplx>::mul(gamma, z);
-                    if (p.has_c) {
-                        const cplx c = p.C[ic + j * p.ldc];
-                        const cplx bc = Elem<cplx>::mul(beta, c);
-                        out.re += bc.re;
-                        out.im += bc.im;
-                    }
+                    const cplx out = Elem<cplx>::mul(gamma, cplx{acc[a][b][2 * h], acc[a][b][2 * h + 1]});
                     if (ic < p.split) p.D2[ic + j * p.ldd2] = out;
                     else p.D[ic + j * p.ldd] = out;
                 }
             }
         }
     } else {
-        const R beta = (R)p.beta.re;
         const R gamma = (R)p.gamma.re;
 #pragma unroll
         for (int a = 0; a < FM; ++a) {
+            const int64_t r = i0 + wm * WM + a * 16 + 4 * q;
+            if (r >= p.M) continue;
 #pragma unroll
             for (int b = 0; b < FN; ++b) {
-                const int64_t j = j0 + wn * WN + b * 16 + cc;
+                const int64_t j = j0 + wn * WN + b * 16 + c16;
                 if (j >= p.N) continue;
-                const int64_t i = i0 + wm * WM + a * 16;
+                R out[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int64_t ii = i + Tr::out_row(q, v);
-                    if (ii >= p.M) continue;
-                    R out = gamma * acc[a][b][v];
-                    if (p.has_c) out = __builtin_fma(beta, p.C[ii + j * p.ldc], out);
-                    if (ii < p.split) p.D2[ii + j * p.ldd2] = out;
-                    else p.D[ii + j * p.ldd] = out;
+                for (int v = 0; v < 4; ++v) out[v] = gamma * acc[a][b][v];
+                if (r + 3 < p.split) {
+                    store_rows4<R>(p.D2, p.ldd2, p.M, r, j, p.d2_vec, out);
+                } else if (r >= p.split) {
+                    store_rows4<R>(p.D, p.ldd, p.M, r, j, p.d_vec, out);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int64_t ii = r + v;
+                        if (ii >= p.M) break;
+                        if (ii < p.split) p.D2[ii + j * p.ldd2] = out[v];
+                        else p.D[ii + j * p.ldd] = out[v];
+                    }
                 }
             }
         }
     }
 }
 
+inline bool aligned16(const void *ptr, int64_t ld, size_t es) {
+    return (reinterpret_cast<uintptr_t>(ptr) % 16) == 0 && ((int64_t)es * ld) % 16 == 0;
+}
+
 template <typename T, int MT, int NT, int KT>
 hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
+    constexpr bool CPLX = GemmTraits<T>::kCplx;
     GemmParams<T> p;
     p.M = g.M;
     p.N = g.N;
@@ -373,18 +482,33 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
     p.D2 = static_cast<T *>(g.D2 ? g.D2 : g.D);
     p.ldd2 = g.D2 ? g.ldd2 : g.ldd;
     p.split = g.D2 ? g.split : 0;
-    p.beta = g.beta;
     p.gamma = g.gamma;
     p.has_c = (g.C != nullptr) && (g.beta.re != 0.0 || g.beta.im != 0.0);
-    constexpr int vecb = 16;
-    const bool cplx_t = GemmTraits<T>::kCplx;
-    p.a_vec = cplx_t ? 1
-                     : ((reinterpret_cast<uintptr_t>(g.A) % vecb) == 0 &&
-                        (g.lda * (int64_t)sizeof(T)) % vecb == 0);
-    p.b_vec = cplx_t ? 1
-                     : ((reinterpret_cast<uintptr_t>(g.Bm) % vecb) == 0 &&
-                        (g.ldb * (int64_t)sizeof(T)) % vecb == 0);
-    const int64_t Mr = cplx_t ? 2 * g.M : g.M;
+    if (g.gamma.re == 0.0 && g.gamma.im == 0.0) {
+        // D = beta * C: no product at all
+        p.K = 0;
+        p.gamma = Scalar{1.0, 0.0};
+        p.sc = g.beta;
+    } else if (CPLX) {
+        // sc = beta / gamma (complex), exact when gamma = +-1
+        const double den = g.gamma.re * g.gamma.re + g.gamma.im * g.gamma.im;
+        if (g.gamma.im == 0.0)
+            p.sc = Scalar{g.beta.re / g.gamma.re, g.beta.im / g.gamma.re};
+        else
+            p.sc = Scalar{(g.beta.re * g.gamma.re + g.beta.im * g.gamma.im) / den,
+                          (g.beta.im * g.gamma.re - g.beta.re * g.gamma.im) / den};
+    } else {
+        p.sc = Scalar{g.beta.re / g.gamma.re, 0.0};
+    }
+    p.extA = p.K > 0 ? (p.K - 1) * p.lda + p.M : 0;
+    p.extB = p.K > 0 ? (p.N - 1) * p.ldb + p.K : 0;
+    const size_t es = sizeof(T);
+    p.a_vec = aligned16(g.A, g.lda, es);
+    p.b_vec = aligned16(g.Bm, g.ldb, es);
+    p.c_vec = p.has_c ? aligned16(g.C, g.ldc, es) : 0;
+    p.d_vec = aligned16(g.D, g.ldd, es);
+    p.d2_vec = aligned16(p.D2, p.ldd2, es);
+    const int64_t Mr = CPLX ? 2 * g.M : g.M;
     const int64_t tM = (Mr + MT - 1) / MT;
     const int64_t tN = (g.N + NT - 1) / NT;
     if (tM <= 0 || tN <= 0) return hipSuccess;
@@ -398,14 +522,28 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Macro tile by launch size: 128 x 128 when that gives at least two tiles
+// per CU (256 CUs), else 64 x 64.
+template <typename T, int KT>
+hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
+    const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
+    const int64_t big = ((Mr + 127) / 128) * ((g.N + 127) / 128);
+    if (big >= 512) return launch_tile<T, 128, 128, KT>(g, st);
+    return launch_tile<T, 64, 64, KT>(g, st);
+}
+
 }  // namespace
 
 hipError_t gemm_launch(int dtype, const GemmDesc &g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    // 32-bit buffer offsets inside one K tile of A and one column tile of Bm
+    const int64_t es = (int64_t)dtype_size(dtype);
+    if (g.lda * es * 32 + 4096 > 0x7fffffffLL || g.ldb * es * 128 + 4096 > 0x7fffffffLL)
+        return hipErrorInvalidValue;
     switch (dtype) {
-        case R32F: return launch_tile<float, 128, 128, 32>(g, stream);
-        case R64F: return launch_tile<double, 128, 128, 16>(g, stream);
-        case C64F: return launch_tile<cplx, 128, 128, 16>(g, stream);
+        case R32F: return launch_sized<float, 32>(g, stream);
+        case R64F: return launch_sized<double, 16>(g, stream);
+        case C64F: return launch_sized<cplx, 16>(g, stream);
         default: return hipErrorInvalidValue;
     }
 }
