@@ -96,46 +96,64 @@ def summarize_kernels(records):
     return out
 
 
-def cpu_baseline(big, small, seconds_hint=10.0):
-    """Time the oracle (as it stands) on a bounded sample of each workload."""
+def cpu_baseline(big, small, seconds=12.0):
+    """Time the oracle (as it stands) on a bounded sample of each workload:
+    about seconds/2 on a block of right-hand-side columns of the large solve
+    (columns are independent, so the sample is a smaller instance of the same
+    work) and about seconds/2 on repeats of the whole batched workload."""
     import oracle
     L4, B4, a4, cfg4 = big
     L2, B2, a2, cfg2 = small
     cores = oracle.num_threads()
-    # big: a block of right-hand-side columns at full m (columns are independent)
-    ncols = 128
+    # calibrate on 64 columns, then size the column block to ~seconds/2
+    t = time.perf_counter()
+    oracle.solve(L4, np.asfortranarray(B4[:, :64]), a4)
+    t64 = max(time.perf_counter() - t, 1e-3)
+    ncols = int(min(cfg4.n, max(64, 64 * (seconds / 2) / t64)))
     t = time.perf_counter()
     oracle.solve(L4, np.asfortranarray(B4[:, :ncols]), a4)
     t_big = time.perf_counter() - t
     fl_big = float(cfg4.m) ** 2 * ncols
-    # small: the whole batch
     t = time.perf_counter()
     oracle.solve_batched(L2, B2, a2)
+    t1 = max(time.perf_counter() - t, 1e-3)
+    reps = int(min(200, max(1, (seconds / 2) / t1)))
+    t = time.perf_counter()
+    for _ in range(reps):
+        oracle.solve_batched(L2, B2, a2)
     t_small = time.perf_counter() - t
-    fl_small = cfg2.flops
-    # scale the big sample up to about `seconds_hint` of CPU work if it was quick
-    reps = max(1, int(seconds_hint / max(t_big + t_small, 1e-3)))
-    reps = min(reps, 8)
-    if reps > 1:
-        t = time.perf_counter()
-        for _ in range(reps - 1):
-            oracle.solve(L4, np.asfortranarray(B4[:, :ncols]), a4)
-            oracle.solve_batched(L2, B2, a2)
-        t_extra = time.perf_counter() - t
-    else:
-        t_extra = 0.0
-    total_t = t_big + t_small + t_extra
-    total_f = (fl_big + fl_small) * reps
+    fl_small = cfg2.flops * reps
     return {
-        "value": total_f / total_t / 1e9,
+        "value": (fl_big + fl_small) / (t_big + t_small) / 1e9,
         "unit": "GFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": (f"{reps} x ({cfg4.name}: {ncols} of {cfg4.n} right-hand-side columns at full m; "
-                   f"{cfg2.name}: all {cfg2.batch} problems), {total_t:.1f} s"),
+        "sample": (f"{cfg4.name}: {ncols} of {cfg4.n} right-hand-side columns at full m "
+                   f"({t_big:.1f} s); {cfg2.name}: the whole batch {reps} times ({t_small:.1f} s)"),
         "big_gflops": fl_big / t_big / 1e9,
         "small_gflops": fl_small / t_small / 1e9,
     }
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch of `kernel_key` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when the summary is missing or
+    was taken on a different version of the kernel's source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["bytes_per_launch"]
 
 
 def main():
@@ -244,7 +262,7 @@ def main():
         "peak": PEAK["fp64_mfma_tflops"],
         "unit": "TFLOP/s",
         "frac": (upd.get("tflops") or 0.0) / PEAK["fp64_mfma_tflops"],
-        "traffic": None,
+        "traffic": measured_traffic("update_gemm_f64"),
         "launches": upd.get("launches"),
         "mean_launch_ms": upd.get("mean_ms"),
     }
