@@ -258,3 +258,57 @@ def test_workspace_allocation_failure_leaves_B_untouched(T, monkeypatch):
     s.synchronize()
     check("f64", from_dev(Bd), oracle.solve(L, B, 1.0), "after failed alloc")
     T.trsm_release_workspace()
+
+
+# ---- the streaming batched kernel (>= 2 tasks per CU, fp64 / complex) -------
+
+@pytest.mark.parametrize("dtype", ["f64", "c64"])
+@pytest.mark.parametrize("batch,m,n", [(600, 64, 64), (600, 1, 64), (600, 17, 5), (520, 33, 100),
+                                       (2100, 64, 64), (300, 48, 130)])
+def test_batched_streaming(T, dtype, batch, m, n):
+    """Enough tasks (problem x 64-column group) for the persistent streaming
+    kernel; ragged m, several column groups, more tasks than waves."""
+    L, B = make_problem(dtype, m, n, seed=batch + 7 * m + n, batch=batch)
+    a = 0.5 - 0.25j if dtype == "c64" else -0.75
+    Ad, Bd = to_dev(L), to_dev(B)
+    T.trsm_lln_strided_batched(Ad, Bd, a)
+    sync()
+    X = from_dev(Bd)
+    ref = oracle.solve_batched(L, B, a)
+    e = max_problem_nrel(X, ref)
+    assert e <= TOL[dtype] and e <= SANITY[dtype], e
+
+
+@pytest.mark.parametrize("dtype", ["f64", "c64"])
+def test_batched_streaming_padded_nan_upper(T, dtype):
+    """Padded leading dimensions, a NaN strict upper triangle and NaN padding
+    in A; B's padding rows must stay untouched."""
+    import torch
+    batch, m, n = 700, 40, 70
+    L, B = make_problem(dtype, m, n, seed=11, batch=batch, lda=m + 3, ldb=m + 5, upper="nan")
+    Ad = to_dev(L, pad=np.nan)
+    Bd = to_dev(B, pad=777.0)
+    T.trsm_lln_strided_batched(Ad, Bd, 1.0)
+    sync()
+    ldb = m + 5
+    full = from_dev(torch.as_strided(Bd, (batch, ldb, n), (Bd.stride(0), 1, ldb)))
+    assert np.all(full[:, m:] == 777.0), "padding rows of B were modified"
+    Lz, _ = make_problem(dtype, m, n, seed=11, batch=batch)
+    ref = oracle.solve_batched(Lz, np.ascontiguousarray(B), 1.0)
+    e = max_problem_nrel(full[:, :m], ref)
+    assert e <= TOL[dtype] and e <= SANITY[dtype], e
+
+
+@pytest.mark.parametrize("dtype", ["f64", "c64"])
+def test_batched_streaming_bidiagonal_exact(T, dtype):
+    """Unit bidiagonal L with -1 below the diagonal on every problem: X is the
+    running column sum of integer B, exact on the streaming path."""
+    batch, m, n = 600, 64, 64
+    L1 = unit_bidiagonal_minus_one(m, dtype)
+    L = np.ascontiguousarray(np.broadcast_to(L1, (batch, m, m)).transpose(0, 2, 1)).transpose(0, 2, 1)
+    Bs = np.stack([small_integer_rhs(m, n, dtype, seed=p) for p in range(batch)])
+    B = np.ascontiguousarray(Bs.transpose(0, 2, 1)).transpose(0, 2, 1)
+    Ad, Bd = to_dev(L), to_dev(B)
+    T.trsm_lln_strided_batched(Ad, Bd, 1.0)
+    sync()
+    assert np.array_equal(from_dev(Bd), np.cumsum(B, axis=1))

@@ -55,22 +55,27 @@ bool log_enabled() {
 // ---- device checks and workspace cache ----------------------------------
 
 std::mutex g_mu;
-std::map<int, bool> g_dev_ok;                                  // device -> is gfx950
+struct DevInfo {
+    bool ok;   // gfx950
+    int cus;   // compute units
+};
+std::map<int, DevInfo> g_dev;                                  // device -> properties
 std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
 
-trsm_status_t check_device(int *dev_out) {
+trsm_status_t check_device(int *dev_out, int *cus_out = nullptr) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
     *dev_out = dev;
     std::lock_guard<std::mutex> lk(g_mu);
-    auto it = g_dev_ok.find(dev);
-    if (it == g_dev_ok.end()) {
+    auto it = g_dev.find(dev);
+    if (it == g_dev.end()) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
         const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-        it = g_dev_ok.emplace(dev, ok).first;
+        it = g_dev.emplace(dev, DevInfo{ok, prop.multiProcessorCount}).first;
     }
-    return it->second ? TRSM_STATUS_SUCCESS : TRSM_STATUS_NOT_SUPPORTED;
+    if (cus_out) *cus_out = it->second.cus;
+    return it->second.ok ? TRSM_STATUS_SUCCESS : TRSM_STATUS_NOT_SUPPORTED;
 }
 
 trsm_status_t get_workspace(int dev, hipStream_t st, size_t bytes, void **out) {

@@ -1,0 +1,230 @@
+// Kernel (a) on the matrix cores: the direct solve of L X = alpha B for
+// m <= 64 in fp64 and complex fp64, one workgroup per (problem, group of 64
+// right-hand-side columns).
+//
+// HSMA-TRSM ("Hierarchical Shared Memory-Aware Optimization for TRSM on GPU
+// Platforms") keeps a small problem on chip and solves it in one thread
+// block (section 4.2.1); its large-regime machinery (section 4.3) inverts
+// the diagonal blocks and turns the rest into matrix products.  On gfx950
+// the whole small problem fits one workgroup's LDS and registers, and the
+// fp64 matrix cores run at the same rate as the fp64 vector units while
+// needing no per-product LDS broadcast, so the small solve is done as the
+// blocked algorithm at 16 x 16 granularity inside one workgroup:
+//
+//   * the lower 16 x 16 blocks of L (ten of them, 40 KB for complex) are
+//     staged in LDS; rows past m become identity rows;
+//   * wave p inverts diagonal block p in place by substitution against the
+//     columns of the identity (section 4.3.1's column-streamed inversion at
+//     16 x 16 scale);
+//   * wave w then owns right-hand-side columns 16w .. 16w+15 of the group,
+//     all 64 rows of them as v_mfma_f64_16x16x4f64 accumulators, and for
+//     p = 0..3 computes X_p = W_p B_p and B_q -= L_qp X_p (q > p) without
+//     further synchronisation: the f64 MFMA result layout (row g + 4v in
+//     item v of lane group g) is exactly the layout of its B operand, so a
+//     solved panel feeds the next products straight from the accumulators;
+//   * complex fp64 uses the real 2x2 embedding (4 real products per complex
+//     product), expanded from the complex LDS blocks when the A fragments
+//     are read.
+// Four waves per workgroup and four workgroups per CU keep sixteen waves
+// per CU, so one workgroup's loads overlap the others' products.
+#include "scalar_ops.h"
+
+namespace trsm {
+namespace {
+
+typedef double d4 __attribute__((ext_vector_type(4)));
+typedef double d2v __attribute__((ext_vector_type(2)));
+
+constexpr int kPanels = 4;  // 16-row panels of the 64 rows
+__host__ __device__ constexpr int blk(int q, int p) { return q * (q + 1) / 2 + p; }
+
+// A fragment for k-step s of the product (output tile a) x (input tile t)
+// with the 16 x 16 block Lb (stored [k][i]); `neg` flips the sign.
+// fp64: MFMA row r stands for block row 4(r % 4) + r / 4, so that item v
+// of lane group g holds block row 4g + v; the k row of a B operand item
+// (4s + g) is block row 4g + s.
+__device__ __forceinline__ double afrag(const double (*Lb)[16], int a, int t, int s, int c, int g,
+                                        double sgn) {
+    (void)a;
+    (void)t;
+    return sgn * Lb[4 * g + s][4 * (c & 3) + (c >> 2)];
+}
+// complex: real row r of an 8-complex-row tile stands for complex row
+// (r % 4) + 4 (r / 8), part (r / 4) % 2; item v of lane group g then holds
+// complex rows g (v = 0, 1: re, im) and g + 4 (v = 2, 3) of the tile.
+__device__ __forceinline__ double afrag(const cplx (*Lb)[16], int a, int t, int s, int c, int g,
+                                        double sgn) {
+    const int i = (c & 3) + 4 * (c >> 3) + 8 * a;
+    const int ri = (c >> 2) & 1;
+    const int k = g + 4 * (s >> 1) + 8 * t;
+    const int ki = s & 1;
+    const cplx z = Lb[k][i];
+    const double v = (ri == ki) ? z.re : (ri ? z.im : -z.im);
+    return sgn * v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64_t ncg,
+                                                         Scalar alpha_s, const T *__restrict__ A,
+                                                         int64_t lda, int64_t strideA,
+                                                         T *__restrict__ B, int64_t ldb,
+                                                         int64_t strideB) {
+    using E = Elem<T>;
+    constexpr bool CPLX = sizeof(T) == 16;
+    constexpr int TILES = CPLX ? 2 : 1;  // 16-real-row MFMA tiles per 16-row panel
+    __shared__ __attribute__((aligned(16))) T Lb[10][16][16];  // block (q,p): [k][i]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = tid >> 6;
+    const int c = lane & 15;
+    const int g = lane >> 4;
+    const int64_t prob = blockIdx.x / ncg;
+    const int64_t cgi = blockIdx.x - prob * ncg;
+    const T *__restrict__ Ap = A + prob * strideA;
+    T *__restrict__ Bp = B + prob * strideB;
+    const int np = (m + 15) >> 4;  // panels that hold rows < m
+
+    // ---- 1. lower blocks of L into LDS (rows >= m: identity) ---------------
+    {
+        const int i = tid & 15, k = tid >> 4;
+#pragma unroll
+        for (int q = 0; q < kPanels; ++q) {
+#pragma unroll
+            for (int p = 0; p <= q; ++p) {
+                const int gi = 16 * q + i, gk = 16 * p + k;
+                T v = E::zero();
+                if (gi < m && gk < m) {
+                    if (gi >= gk) v = Ap[gi + (int64_t)gk * lda];
+                } else if (gi == gk) {
+                    v = E::one();
+                }
+                Lb[blk(q, p)][k][i] = v;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 2. wave w inverts diagonal block w in place -----------------------
+    // The pivots' reciprocals are computed in parallel (lane k, one each) and
+    // stored over the diagonal, so the substitution itself only multiplies.
+    if (w < np) {
+        T(*D)[16] = Lb[blk(w, w)];
+        if (lane < 16) D[lane][lane] = E::recip(D[lane][lane]);
+        const int j = c;  // column of the inverse (lane groups compute copies)
+        T x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == j) ? E::one() : E::zero();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            x[k] = E::mul(x[k], D[k][k]);
+#pragma unroll
+            for (int i = k + 1; i < 16; ++i) x[i] = E::msub(x[i], D[k][i], x[k]);
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) D[j][i] = x[i];
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. this wave's 16 columns, all rows, into accumulators ----------
+    const int64_t col = cgi * 64 + w * 16 + c;
+    const bool colok = col < n;
+    T *__restrict__ Bc = Bp + col * ldb;
+    d4 acc[kPanels][TILES];
+#pragma unroll
+    for (int p = 0; p < kPanels; ++p) {
+#pragma unroll
+        for (int a = 0; a < TILES; ++a) {
+            if constexpr (CPLX) {
+                const int r0 = 16 * p + 8 * a + g;  // complex rows r0 and r0 + 4
+                cplx z0{0.0, 0.0}, z1{0.0, 0.0};
+                if (colok && r0 < m) z0 = Bc[r0];
+                if (colok && r0 + 4 < m) z1 = Bc[r0 + 4];
+                acc[p][a] = d4{z0.re, z0.im, z1.re, z1.im};
+            } else {
+                const int r0 = 16 * p + 4 * g;  // rows r0 .. r0 + 3
+                double v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (colok && r0 + e < m) ? Bc[r0 + e] : 0.0;
+                acc[p][a] = d4{v[0], v[1], v[2], v[3]};
+            }
+        }
+    }
+
+    // ---- 4. X_p = W_p B_p, B_q -= L_qp X_p --------------------------------
+    const T alpha = E::from(alpha_s);
+#pragma unroll
+    for (int p = 0; p < kPanels; ++p) {
+        if (p < np) {  // uniform
+        d4 x[TILES];
+#pragma unroll
+        for (int a = 0; a < TILES; ++a) {
+            x[a] = d4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int t = 0; t < TILES; ++t)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    x[a] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                        afrag(Lb[blk(p, p)], a, t, s, c, g, 1.0), acc[p][t][s], x[a], 0, 0, 0);
+        }
+        // store alpha * X_p
+#pragma unroll
+        for (int a = 0; a < TILES; ++a) {
+            if constexpr (CPLX) {
+                const int r0 = 16 * p + 8 * a + g;
+                if (colok && r0 < m) Bc[r0] = E::mul(alpha, cplx{x[a][0], x[a][1]});
+                if (colok && r0 + 4 < m) Bc[r0 + 4] = E::mul(alpha, cplx{x[a][2], x[a][3]});
+            } else {
+                const int r0 = 16 * p + 4 * g;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (colok && r0 + e < m) Bc[r0 + e] = alpha * x[a][e];
+            }
+        }
+        // update the panels below
+#pragma unroll
+        for (int q = p + 1; q < kPanels; ++q) {
+            if (q < np) {  // uniform
+#pragma unroll
+            for (int a = 0; a < TILES; ++a)
+#pragma unroll
+                for (int t = 0; t < TILES; ++t)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc[q][a] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                            afrag(Lb[blk(q, p)], a, t, s, c, g, -1.0), x[t][s], acc[q][a], 0, 0, 0);
+            }
+        }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t small_mfma_launch(int dtype, int m, int64_t n, Scalar alpha, const void *A,
+                             int64_t lda, int64_t strideA, void *B, int64_t ldb, int64_t strideB,
+                             int64_t batch, hipStream_t stream) {
+    if (m < 1 || m > 64) return hipErrorInvalidValue;
+    const int64_t ncg = (n + 63) / 64;
+    const int64_t nblk = ncg * batch;
+    if (nblk <= 0) return hipSuccess;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    switch (dtype) {
+        case R64F:
+            hipLaunchKernelGGL((small_mfma_kernel<double>), dim3((unsigned)nblk), dim3(256), 0, stream, m, n,
+                               ncg, alpha, static_cast<const double *>(A), lda, strideA,
+                               static_cast<double *>(B), ldb, strideB);
+            break;
+        case C64F:
+            hipLaunchKernelGGL((small_mfma_kernel<cplx>), dim3((unsigned)nblk), dim3(256), 0, stream, m, n,
+                               ncg, alpha, static_cast<const cplx *>(A), lda, strideA,
+                               static_cast<cplx *>(B), ldb, strideB);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace trsm

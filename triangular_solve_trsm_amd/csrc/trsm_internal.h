@@ -26,11 +26,16 @@ struct Scalar {
     double re, im;
 };
 
-// ---- kernel (a): single-workgroup direct solve, m <= 64 ------------------
-// One workgroup per (problem, group of 64 right-hand-side columns).
+// ---- kernel (a): direct solve, m <= 64 -----------------------------------
+// One workgroup per (problem, group of 64 right-hand-side columns): fp64 and
+// complex fp64 on the matrix cores (small_mfma_launch), fp32 with one
+// 16-row panel per wave on the vector units.
 hipError_t small_lln_launch(int dtype, int m, int64_t n, Scalar alpha, const void *A,
                             int64_t lda, int64_t strideA, void *B, int64_t ldb,
                             int64_t strideB, int64_t batch, hipStream_t stream);
+hipError_t small_mfma_launch(int dtype, int m, int64_t n, Scalar alpha, const void *A,
+                             int64_t lda, int64_t strideA, void *B, int64_t ldb,
+                             int64_t strideB, int64_t batch, hipStream_t stream);
 
 // ---- kernel (b1): inversion of every ib x ib diagonal block ---------------
 // W receives ceil(m/ib) blocks, block t at W + t*ib*ib (column-major, ld ib),
