@@ -13,9 +13,9 @@
 //
 //   * the lower 16 x 16 blocks of L (ten of them, 40 KB for complex) are
 //     staged in LDS; rows past m become identity rows;
-//   * wave p inverts diagonal block p in place by substitution against the
-//     columns of the identity (section 4.3.1's column-streamed inversion at
-//     16 x 16 scale);
+//   * one wave inverts the four diagonal blocks in place (lane group g takes
+//     block g) by substitution against the columns of the identity (section
+//     4.3.1's column-streamed inversion at 16 x 16 scale);
 //   * wave w then owns right-hand-side columns 16w .. 16w+15 of the group,
 //     all 64 rows of them as v_mfma_f64_16x16x4f64 accumulators, and for
 //     p = 0..3 computes X_p = W_p B_p and B_q -= L_qp X_p (q > p) without
@@ -105,26 +105,24 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
     }
     __syncthreads();
 
-    // ---- 2. wave w inverts diagonal block w in place -----------------------
-    // The pivots' reciprocals are computed in parallel (lane k, one each) and
-    // stored over the diagonal, so the substitution itself only multiplies.
-    if (w < np) {
-        T(*D)[16] = Lb[blk(w, w)];
-        if (lane < 16) D[lane][lane] = E::recip(D[lane][lane]);
-        const int j = c;  // column of the inverse (lane groups compute copies)
+    // ---- 2. wave 0 inverts the diagonal blocks in place --------------------
+    // Lane group g takes block g, lane c of it column c of the inverse.  The
+    // pivots' reciprocals are computed first (one per lane) and stored over
+    // the diagonal, so the substitution itself only multiplies.
+    if (w == 0 && g < np) {
+        T(*D)[16] = Lb[blk(g, g)];
+        D[c][c] = E::recip(D[c][c]);
         T x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == j) ? E::one() : E::zero();
+        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? E::one() : E::zero();
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             x[k] = E::mul(x[k], D[k][k]);
 #pragma unroll
             for (int i = k + 1; i < 16; ++i) x[i] = E::msub(x[i], D[k][i], x[k]);
         }
-        if (g == 0) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) D[j][i] = x[i];
-        }
+        for (int i = 0; i < 16; ++i) D[c][i] = x[i];
     }
     __syncthreads();
 
@@ -163,7 +161,7 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
         for (int a = 0; a < TILES; ++a) {
             x[a] = d4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int t = 0; t < TILES; ++t)
+            for (int t = 0; t <= a; ++t)  // W_p is lower triangular: tile (0, 1) is zero
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
                     x[a] = __builtin_amdgcn_mfma_f64_16x16x4f64(
