@@ -1,0 +1,73 @@
+// Raw buffer loads for gfx950 kernels: a load at or past the end of the
+// described range returns zero without a branch, so ragged edges cost no
+// control flow.  Internal to the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace trsm {
+
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource of a gfx9-family part (gfx950): base address, no
+// stride, a byte range (loads at or past it return 0), 32-bit data format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const uint32_t n =
+        bytes >= 0xffffffffLL ? 0xffffffffu : (bytes <= 0 ? 0u : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                             0x00020000);
+}
+
+// 16 bytes at byte offset `off`; `vec` says the address is 16-byte aligned,
+// otherwise four dword loads are used (every element type here is at least
+// dword aligned).
+__device__ __forceinline__ u4v ld16(__amdgpu_buffer_rsrc_t r, uint32_t off, int vec) {
+    if (vec) return __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    u4v v;
+    v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    v[1] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4, 0, 0);
+    v[2] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 8, 0, 0);
+    v[3] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 12, 0, 0);
+    return v;
+}
+
+// N consecutive elements of T at byte offset `off` into dst, as 16-byte
+// loads where N * sizeof(T) allows it and dword loads otherwise.
+template <typename T, int N>
+__device__ __forceinline__ void ld_elems(__amdgpu_buffer_rsrc_t r, uint32_t off, int vec,
+                                         T (&dst)[N]) {
+    constexpr int NB = N * (int)sizeof(T);
+    static_assert(NB % 4 == 0, "dword multiple");
+    if constexpr (NB % 16 == 0) {
+        constexpr int PER = 16 / (int)sizeof(T);
+#pragma unroll
+        for (int q = 0; q < NB / 16; ++q) {
+            const u4v v = ld16(r, off + 16 * q, vec);
+            // Bit-cast the whole vector to a vector of T and index that: a
+            // bit cast of each u4v element on its own was compiled as a
+            // repeat of element 0 (seen with hipcc for gfx950).
+            if constexpr (sizeof(T) == 4) {
+                typedef T v4t __attribute__((ext_vector_type(4)));
+                const v4t w = __builtin_bit_cast(v4t, v);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) dst[q * PER + e] = w[e];
+            } else if constexpr (sizeof(T) == 8) {
+                typedef T v2t __attribute__((ext_vector_type(2)));
+                const v2t w = __builtin_bit_cast(v2t, v);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) dst[q * PER + e] = w[e];
+            } else {
+                dst[q] = __builtin_bit_cast(T, v);
+            }
+        }
+    } else {
+        unsigned w[NB / 4];
+#pragma unroll
+        for (int q = 0; q < NB / 4; ++q)
+            w[q] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * q, 0, 0);
+        __builtin_memcpy(dst, w, NB);
+    }
+}
+
+}  // namespace trsm

@@ -17,13 +17,15 @@
 //     reciprocal of d_kk; the P solved values are broadcast to the wave with
 //     v_readlane (SGPR operands of the following FMAs); every lane subtracts
 //     d_ik * x_k from its rows i > k;
-//   * column k of D_t is read straight into VGPRs, each lane its own rows,
-//     and column k+1 is prefetched into a second register set while column k
-//     is used -- the two-buffer alternation of Figure 7, held in registers
-//     (the CDNA4 register file is 512 KB per CU) instead of shared memory;
-//     LDS is not used at all, so the footprint is O(ib) per wavefront.
+//   * column k of D_t is read straight into VGPRs, each lane its own rows.
+//     Figure 7 alternates two column buffers (compute one, fetch the next);
+//     here the buffers are a ring of several columns in registers (the CDNA4
+//     register file is 512 KB per CU), because one column ahead is far less
+//     than the memory latency at a few hundred cycles per step.  LDS is not
+//     used at all, so the footprint stays O(ib) per wavefront.
 // Rows above the diagonal are written as explicit zeros, which the triangular
 // GEMM of the solve phase relies on.
+#include "buffer_ops.h"
 #include "scalar_ops.h"
 
 namespace trsm {
@@ -54,13 +56,25 @@ constexpr int panel_cols() {
     return p < ib ? p : ib;
 }
 
+// Columns of D in flight: a ring of DP columns (R values of T per lane each)
+// within 128 VGPRs, between 2 and 16.  At a few hundred cycles per step,
+// several columns ahead cover the memory latency that one column ahead left
+// exposed on every step.
+template <typename T, int R>
+constexpr int ring_cols() {
+    constexpr int d = 128 / (R * words<T>());
+    return d < 2 ? 2 : (d > 16 ? 16 : d);
+}
+
 template <typename T, int R>
 __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__restrict__ A,
                                                       int64_t lda, T *__restrict__ W,
-                                                      int npanels) {
+                                                      int npanels, int vec) {
     using E = Elem<T>;
     constexpr int IB = 64 * R;
     constexpr int P = panel_cols<T, R>();
+    constexpr int DP = ring_cols<T, R>();
+    constexpr int U = DP > R ? DP : R;  // steps per unrolled group (multiple of both)
     const int t = blockIdx.x / npanels;
     const int c = blockIdx.x - t * npanels;
     const int lane = threadIdx.x;
@@ -68,57 +82,62 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
     const int bs = (int)((m - base) < IB ? (m - base) : IB);
     const int j0 = c * P;
     if (j0 >= bs) return;
-    const T *__restrict__ D = A + base + base * lda;  // D(i, k) = D[i + k*lda]
     T *__restrict__ Wt = W + (int64_t)t * IB * IB;
+    // D(i, k) at element i + k * lda from here; reads past A's last element
+    // return zero (they only reach rows and columns >= bs, which are unused).
+    const int64_t doff = base + base * lda;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(A + doff, ((m - 1) + (m - 1) * lda + 1 - doff) * (int64_t)sizeof(T));
+    const int row0 = lane * R;  // this lane's rows row0 .. row0 + R - 1
+    auto col_off = [&](int k) -> uint32_t {
+        return (uint32_t)(((int64_t)row0 + (int64_t)k * lda) * (int64_t)sizeof(T));
+    };
 
     // identity tile E_j for columns j0 .. j0+P-1, and reciprocals of own pivots
     T x[R][P];
     T inv[R];
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-        const int i = lane * R + rr;
-        inv[rr] = (i < bs) ? E::recip(D[i + (int64_t)i * lda]) : E::zero();
+        const int i = row0 + rr;
+        T d[1];
+        ld_elems<T, 1>(rs, (uint32_t)(((int64_t)i + (int64_t)i * lda) * (int64_t)sizeof(T)), 0, d);
+        inv[rr] = E::recip(d[0]);
 #pragma unroll
-        for (int jj = 0; jj < P; ++jj) x[rr][jj] = (i == j0 + jj) ? E::one() : E::zero();
+        for (int jj = 0; jj < P; ++jj) x[rr][jj] = E::sel(i == j0 + jj, E::one(), E::zero());
     }
 
-    // column k of D for own rows i > k (strict lower part only)
-    auto load_col = [&](int k, T *dst) {
+    // Steps run in groups of U starting at a multiple of U, so that the
+    // pivot row inside its lane (k % R) and the ring slot (k % DP) are
+    // compile-time indices; steps before j0 are skipped.  Column loads are
+    // unconditional, so the compiler can keep DP of them in flight.
+    const int k_begin = (j0 / U) * U;
+    T ring[DP][R];
 #pragma unroll
-        for (int rr = 0; rr < R; ++rr) {
-            const int i = lane * R + rr;
-            dst[rr] = (k < bs && i > k && i < bs) ? D[i + (int64_t)k * lda] : E::zero();
-        }
-    };
-
-    T dnext[R];
-    load_col(j0, dnext);
-    const int kb_first = j0 / R;
-    const int kb_last = (bs - 1) / R;
-    for (int kb = kb_first; kb <= kb_last; ++kb) {  // kb = lane owning rows kb*R ..
+    for (int u = 0; u < DP; ++u) ld_elems<T, R>(rs, col_off(k_begin + u), vec, ring[u]);
+    for (int k0 = k_begin; k0 < bs; k0 += U) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int k = kb * R + r;
-            if (k < j0) continue;  // wave-uniform
-            if (k >= bs) break;    // wave-uniform
-            T dcur[R];
+        for (int u = 0; u < U; ++u) {
+            const int k = k0 + u;
+            const int slot = u % DP;
+            const int r = u % R;
+            if (k >= j0 && k < bs) {  // wave-uniform
+                const int kb = k / R;  // lane owning row k
+                T s[P];
 #pragma unroll
-            for (int rr = 0; rr < R; ++rr) dcur[rr] = dnext[rr];
-            load_col(k + 1, dnext);  // prefetch the next column
-            T s[P];
+                for (int jj = 0; jj < P; ++jj) s[jj] = bcast(E::mul(x[r][jj], inv[r]), kb);
+                // rows below the pivot: x_i -= d_ik s (d masked to 0 for i <= k)
 #pragma unroll
-            for (int jj = 0; jj < P; ++jj) s[jj] = bcast(E::mul(x[r][jj], inv[r]), kb);
+                for (int rr = 0; rr < R; ++rr) {
+                    const T d = E::sel(row0 + rr > k, ring[slot][rr], E::zero());
 #pragma unroll
-            for (int rr = 0; rr < R; ++rr) {
-                const int i = lane * R + rr;
-                if (i == k) {
-#pragma unroll
-                    for (int jj = 0; jj < P; ++jj) x[rr][jj] = s[jj];
-                } else if (i > k) {
-#pragma unroll
-                    for (int jj = 0; jj < P; ++jj) x[rr][jj] = E::msub(x[rr][jj], dcur[rr], s[jj]);
+                    for (int jj = 0; jj < P; ++jj) x[rr][jj] = E::msub(x[rr][jj], d, s[jj]);
                 }
+                // the pivot row itself takes the solved values
+                const bool own = lane == kb;
+#pragma unroll
+                for (int jj = 0; jj < P; ++jj) x[r][jj] = E::sel(own, s[jj], x[r][jj]);
             }
+            ld_elems<T, R>(rs, col_off(k + DP), vec, ring[slot]);  // refill the slot just used
         }
     }
 
@@ -128,7 +147,7 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
         if (j >= bs) break;
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
-            const int i = lane * R + rr;
+            const int i = row0 + rr;
             if (i < bs) Wt[i + (int64_t)j * IB] = x[rr][jj];
         }
     }
@@ -143,8 +162,12 @@ hipError_t launch_r(int64_t m, const void *A, int64_t lda, void *W, hipStream_t 
     const int64_t grid = nb * npanels;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // 32-bit buffer offsets reach one diagonal block: IB columns of lda
+    if ((int64_t)sizeof(T) * (lda + 1) * IB > 0x7fffffffLL) return hipErrorInvalidValue;
+    const int vec = (reinterpret_cast<uintptr_t>(A) % 16 == 0) &&
+                    ((int64_t)sizeof(T) * lda) % 16 == 0;
     hipLaunchKernelGGL((diag_inv_kernel<T, R>), dim3((unsigned)grid), dim3(64), 0, st, m,
-                       static_cast<const T *>(A), lda, static_cast<T *>(W), npanels);
+                       static_cast<const T *>(A), lda, static_cast<T *>(W), npanels, vec);
     return hipGetLastError();
 }
 

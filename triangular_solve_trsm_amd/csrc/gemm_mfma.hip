@@ -50,6 +50,7 @@
 //     XCD cover roughly 8 x 8 tiles, sharing the A and Bm panels in its L2.
 #include <type_traits>
 
+#include "buffer_ops.h"
 #include "scalar_ops.h"
 
 namespace trsm {
@@ -58,30 +59,6 @@ namespace {
 typedef double d4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef double d2v __attribute__((ext_vector_type(2)));
-typedef unsigned u4v __attribute__((ext_vector_type(4)));
-
-// Raw buffer resource of a gfx9-family part (gfx950): base address, no
-// stride, a byte range (loads at or past it return 0), 32-bit data format.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
-    const uint32_t n =
-        bytes >= 0xffffffffLL ? 0xffffffffu : (bytes <= 0 ? 0u : (uint32_t)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
-                                             0x00020000);
-}
-
-// 16 bytes at byte offset `off`; `vec` says the address is 16-byte aligned,
-// otherwise four dword loads are used (every element type here is at least
-// dword aligned).
-__device__ __forceinline__ u4v ld16(__amdgpu_buffer_rsrc_t r, uint32_t off, int vec) {
-    if (vec) return __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    u4v v;
-    v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-    v[1] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4, 0, 0);
-    v[2] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 8, 0, 0);
-    v[3] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 12, 0, 0);
-    return v;
-}
-
 template <typename T> struct GemmTraits;
 template <> struct GemmTraits<float> {
     using R = float;

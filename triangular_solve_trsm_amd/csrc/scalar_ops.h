@@ -21,6 +21,7 @@ template <> struct Elem<float> {
         return __builtin_fmaf(-l, x, b);
     }
     __device__ __forceinline__ static float recip(float d) { return 1.0f / d; }
+    __device__ __forceinline__ static float sel(bool c, float a, float b) { return c ? a : b; }
 };
 
 template <> struct Elem<double> {
@@ -34,6 +35,7 @@ template <> struct Elem<double> {
         return __builtin_fma(-l, x, b);
     }
     __device__ __forceinline__ static double recip(double d) { return 1.0 / d; }
+    __device__ __forceinline__ static double sel(bool c, double a, double b) { return c ? a : b; }
 };
 
 template <> struct Elem<cplx> {
@@ -60,6 +62,10 @@ template <> struct Elem<cplx> {
         if (d.im == 0.0) return cplx{1.0 / d.re, 0.0};
         double den = d.re * d.re + d.im * d.im;
         return cplx{d.re / den, -d.im / den};
+    }
+    // c ? a : b, part by part (keeps the values in registers)
+    __device__ __forceinline__ static cplx sel(bool c, cplx a, cplx b) {
+        return cplx{c ? a.re : b.re, c ? a.im : b.im};
     }
 };
 
