@@ -1,0 +1,112 @@
+"""Offline block-size profiling for the blocked path; writes csrc/ib_table.inc.
+
+The adaptive blocking of HSMA-TRSM ("Hierarchical Shared Memory-Aware
+Optimization for TRSM on GPU Platforms", section 4.3.2, Figure 8) has two
+phases: offline, every candidate block size is timed for each (matrix scale,
+data type) and only the fastest is kept in a table; online, the library looks
+up the entry of the nearest tabulated scale.  This script is the offline
+phase for MI355X; the online lookup is trsm_lln_select_ib in the library.
+
+Protocol (section 5.1 of the pages): square problems (m = n), inputs drawn by
+trsm_inputs, each point run 10 times, the first discarded, the mean of the
+last 9 kept.  B is restored from a pristine copy before every run, outside
+the timed region.
+
+Usage (on an MI355X, library built):
+    python triangular_solve_trsm_amd/tune_ib.py [--sizes 128,256,...] [--out PATH]
+then rebuild the library so that the new table is compiled in.
+"""
+from __future__ import annotations
+
+import argparse
+import datetime
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+CANDIDATES = (64, 128, 256, 512)
+DTYPES = (("f32", "R32F"), ("f64", "R64F"), ("c64", "C64F"))
+DEFAULT_SIZES = (128, 256, 512, 1024, 2048, 4096, 8192, 16384)
+
+
+def time_point(T, torch, L, B, alpha, ib, runs=10):
+    import numpy as np
+    Ad = torch.from_numpy(np.ascontiguousarray(L.T)).cuda().T
+    B0 = torch.from_numpy(np.ascontiguousarray(B.T)).cuda().T
+    Bd = B0.clone()
+    times = []
+    for _ in range(runs):
+        Bd.copy_(B0)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        T.trsm_lln_ex(Ad, Bd, alpha, ib=ib, force_blocked=True)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return sum(times[1:]) / (runs - 1)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--sizes", default=",".join(str(s) for s in DEFAULT_SIZES))
+    ap.add_argument("--out", default=os.path.join(HERE, "csrc", "ib_table.inc"))
+    ap.add_argument("--json", default=None, help="also write every timing to this file")
+    args = ap.parse_args()
+    sizes = [int(s) for s in args.sizes.split(",") if s]
+
+    import torch
+    import triangular_solve_trsm_amd as T
+    from trsm_inputs import make_problem
+
+    assert torch.cuda.is_available(), "the sweep runs on the GPU"
+    props = torch.cuda.get_device_properties(0)
+    device = f"{getattr(props, 'gcnArchName', props.name)} ({props.multi_processor_count} CUs)"
+    results = []
+    best = {}
+    for dt, code in DTYPES:
+        for m in sizes:
+            L, B = make_problem(dt, m, m, seed=20261300 + m)
+            alpha = 1.0 + 0j if dt == "c64" else 1.0
+            row = {}
+            for ib in CANDIDATES:
+                if ib > m:
+                    continue
+                ms = time_point(T, torch, L, B, alpha, ib)
+                row[ib] = ms
+                results.append({"dtype": dt, "m": m, "ib": ib, "ms": ms})
+                print(json.dumps(results[-1]), flush=True)
+            ib_best = min(row, key=row.get)
+            best[(code, m)] = (ib_best, row)
+            del L, B
+            torch.cuda.empty_cache()
+
+    stamp = datetime.date.today().isoformat()
+    lines = [
+        "// Diagonal block size by (data type, matrix order), used with a",
+        "// nearest-order match (section 4.3.2 of the pages: offline profiling,",
+        "// online lookup).  Written by triangular_solve_trsm_amd/tune_ib.py on",
+        f"// {device}, {stamp}: square problems, mean of runs 2-10 per point.",
+        "// Each entry's comment lists the time in ms of every candidate.",
+        "static const IbEntry kIbTable[] = {",
+    ]
+    for (code, m), (ib, row) in best.items():
+        times = ", ".join(f"{c}: {row[c]:.3f}" for c in sorted(row))
+        lines.append(f"    {{{code}, {m}, {ib}}},  // {times}")
+    lines.append("};")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {args.out}", flush=True)
+    if args.json:
+        with open(args.json, "w") as f:
+            json.dump(results, f, indent=1)
+
+
+if __name__ == "__main__":
+    main()
