@@ -10,7 +10,8 @@
 // fetched while the current one is used (double buffering).
 //
 // gfx950 mapping (one wavefront per workgroup, no barriers):
-//   * workgroup (t, c) computes columns [c*P, c*P + P) of W_t = D_t^{-1};
+//   * task (t, c) computes columns [c*P, c*P + P) of W_t = D_t^{-1}; the
+//     tasks of one block run on one XCD, sharing its L2;
 //   * lane l owns rows l*R .. l*R + R - 1 (R = ib/64) of those P columns, as
 //     R x P values in VGPRs (the identity tile is generated in registers);
 //   * step k (k = c*P .. bs-1): the lane owning row k scales its row by the
@@ -75,8 +76,15 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
     constexpr int P = panel_cols<T, R>();
     constexpr int DP = ring_cols<T, R>();
     constexpr int U = DP > R ? DP : R;  // steps per unrolled group (multiple of both)
-    const int t = blockIdx.x / npanels;
-    const int c = blockIdx.x - t * npanels;
+    // Workgroups go round-robin to the 8 XCDs (workgroup b on XCD b % 8);
+    // give each XCD a contiguous run of (block, panel) tasks so that the
+    // waves reading one diagonal block share that XCD's L2.
+    const int total = (int)((m + IB - 1) / IB) * npanels;
+    const int per = (total + 7) / 8;
+    const int q = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (q >= total) return;
+    const int t = q / npanels;
+    const int c = q - t * npanels;
     const int lane = threadIdx.x;
     const int64_t base = (int64_t)t * IB;
     const int bs = (int)((m - base) < IB ? (m - base) : IB);
@@ -159,9 +167,10 @@ hipError_t launch_r(int64_t m, const void *A, int64_t lda, void *W, hipStream_t 
     constexpr int P = panel_cols<T, R>();
     const int64_t nb = (m + IB - 1) / IB;
     const int npanels = (IB + P - 1) / P;
-    const int64_t grid = nb * npanels;
-    if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int64_t total = nb * npanels;
+    if (total <= 0) return hipSuccess;
+    if (total > 0x7fffffffLL - 8) return hipErrorInvalidConfiguration;
+    const int64_t grid = 8 * ((total + 7) / 8);  // whole rounds over the 8 XCDs
     // 32-bit buffer offsets reach one diagonal block: IB columns of lda
     if ((int64_t)sizeof(T) * (lda + 1) * IB > 0x7fffffffLL) return hipErrorInvalidValue;
     const int vec = (reinterpret_cast<uintptr_t>(A) % 16 == 0) &&
