@@ -19,31 +19,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
                                              0x00020000);
 }
 
-// 16 bytes at byte offset `off`; `vec` says the address is 16-byte aligned,
-// otherwise four dword loads are used (every element type here is at least
-// dword aligned).
-__device__ __forceinline__ u4v ld16(__amdgpu_buffer_rsrc_t r, uint32_t off, int vec) {
-    if (vec) return __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    u4v v;
-    v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-    v[1] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4, 0, 0);
-    v[2] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 8, 0, 0);
-    v[3] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 12, 0, 0);
-    return v;
+// 16 bytes at byte offset `off`.  VEC: the address is 16-byte aligned and
+// one 16-byte load is used; otherwise four dword loads (every element type
+// here is at least dword aligned).  VEC is a template parameter on purpose:
+// with a run-time choice the two paths meet in a register copy, and the copy
+// makes the compiler wait for the load at once, which defeats prefetching.
+template <bool VEC>
+__device__ __forceinline__ u4v ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (VEC) {
+        return __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    } else {
+        u4v v;
+        v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+        v[1] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4, 0, 0);
+        v[2] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 8, 0, 0);
+        v[3] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 12, 0, 0);
+        return v;
+    }
 }
 
 // N consecutive elements of T at byte offset `off` into dst, as 16-byte
 // loads where N * sizeof(T) allows it and dword loads otherwise.
-template <typename T, int N>
-__device__ __forceinline__ void ld_elems(__amdgpu_buffer_rsrc_t r, uint32_t off, int vec,
-                                         T (&dst)[N]) {
+template <typename T, int N, bool VEC>
+__device__ __forceinline__ void ld_elems(__amdgpu_buffer_rsrc_t r, uint32_t off, T (&dst)[N]) {
     constexpr int NB = N * (int)sizeof(T);
     static_assert(NB % 4 == 0, "dword multiple");
     if constexpr (NB % 16 == 0) {
         constexpr int PER = 16 / (int)sizeof(T);
 #pragma unroll
         for (int q = 0; q < NB / 16; ++q) {
-            const u4v v = ld16(r, off + 16 * q, vec);
+            const u4v v = ld16<VEC>(r, off + 16 * q);
             // Bit-cast the whole vector to a vector of T and index that: a
             // bit cast of each u4v element on its own was compiled as a
             // repeat of element 0 (seen with hipcc for gfx950).

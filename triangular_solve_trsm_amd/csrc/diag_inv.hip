@@ -67,10 +67,10 @@ constexpr int ring_cols() {
     return d < 2 ? 2 : (d > 16 ? 16 : d);
 }
 
-template <typename T, int R>
+template <typename T, int R, bool VEC>
 __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__restrict__ A,
                                                       int64_t lda, T *__restrict__ W,
-                                                      int npanels, int vec) {
+                                                      int npanels) {
     using E = Elem<T>;
     constexpr int IB = 64 * R;
     constexpr int P = panel_cols<T, R>();
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
     for (int rr = 0; rr < R; ++rr) {
         const int i = row0 + rr;
         T d[1];
-        ld_elems<T, 1>(rs, (uint32_t)(((int64_t)i + (int64_t)i * lda) * (int64_t)sizeof(T)), 0, d);
+        ld_elems<T, 1, false>(rs, (uint32_t)(((int64_t)i + (int64_t)i * lda) * (int64_t)sizeof(T)), d);
         inv[rr] = E::recip(d[0]);
 #pragma unroll
         for (int jj = 0; jj < P; ++jj) x[rr][jj] = E::sel(i == j0 + jj, E::one(), E::zero());
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
     const int k_begin = (j0 / U) * U;
     T ring[DP][R];
 #pragma unroll
-    for (int u = 0; u < DP; ++u) ld_elems<T, R>(rs, col_off(k_begin + u), vec, ring[u]);
+    for (int u = 0; u < DP; ++u) ld_elems<T, R, VEC>(rs, col_off(k_begin + u), ring[u]);
     for (int k0 = k_begin; k0 < bs; k0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
 #pragma unroll
                 for (int jj = 0; jj < P; ++jj) x[r][jj] = E::sel(own, s[jj], x[r][jj]);
             }
-            ld_elems<T, R>(rs, col_off(k + DP), vec, ring[slot]);  // refill the slot just used
+            ld_elems<T, R, VEC>(rs, col_off(k + DP), ring[slot]);  // refill the slot just used
         }
     }
 
@@ -175,8 +175,12 @@ hipError_t launch_r(int64_t m, const void *A, int64_t lda, void *W, hipStream_t 
     if ((int64_t)sizeof(T) * (lda + 1) * IB > 0x7fffffffLL) return hipErrorInvalidValue;
     const int vec = (reinterpret_cast<uintptr_t>(A) % 16 == 0) &&
                     ((int64_t)sizeof(T) * lda) % 16 == 0;
-    hipLaunchKernelGGL((diag_inv_kernel<T, R>), dim3((unsigned)grid), dim3(64), 0, st, m,
-                       static_cast<const T *>(A), lda, static_cast<T *>(W), npanels, vec);
+    if (vec)
+        hipLaunchKernelGGL((diag_inv_kernel<T, R, true>), dim3((unsigned)grid), dim3(64), 0, st, m,
+                           static_cast<const T *>(A), lda, static_cast<T *>(W), npanels);
+    else
+        hipLaunchKernelGGL((diag_inv_kernel<T, R, false>), dim3((unsigned)grid), dim3(64), 0, st, m,
+                           static_cast<const T *>(A), lda, static_cast<T *>(W), npanels);
     return hipGetLastError();
 }
 

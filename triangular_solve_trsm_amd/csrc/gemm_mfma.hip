@@ -175,7 +175,9 @@ __device__ __forceinline__ void store_rows4(R *X, int64_t ld, int64_t lim, int64
 
 // TRI: A is lower triangular (the solve GEMM); a separate instantiation so
 // that the solve and the update appear as distinct kernels in traces.
-template <typename T, int MT, int NT, int KT, bool TRI>
+// VEC: A and Bm columns are 16-byte aligned (16-byte loads); otherwise the
+// loads are split into dwords.
+template <typename T, int MT, int NT, int KT, bool TRI, bool VEC>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     using Tr = GemmTraits<T>;
     using R = typename Tr::R;
@@ -272,6 +274,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     u4v ra[A_PASSES];
     u4v rb[B_PASSES];
 
+    // Loads of K tile kt into registers.  The ragged-K mask is applied when
+    // the registers are written to LDS (store_tiles), not here: a select on
+    // the loaded values would make the compiler wait for the loads right
+    // after issuing them, before the MFMAs they are meant to overlap.
     auto load_tiles = [&](int kt) {
         const int64_t k0 = (int64_t)kt * KT;  // real k offset
         const int64_t k0t = CPLX ? k0 / 2 : k0;
@@ -284,9 +290,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
                 const int kk = flat / A_TPC;
                 const int rr = flat - kk * A_TPC;
                 const uint32_t boff = (uint32_t)(((int64_t)rr * AU + (int64_t)kk * p.lda) * (int64_t)sizeof(T));
-                u4v v = ld16(rs, boff, p.a_vec);
-                if (k0t + kk >= p.K) v = u4v{0u, 0u, 0u, 0u};
-                ra[s] = v;
+                ra[s] = ld16<VEC>(rs, boff);
             }
         }
         {
@@ -299,31 +303,40 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
                 const int kv = (flat - jj * B_TPC) * VR;  // real k inside the tile
                 const int64_t kvt = CPLX ? kv / 2 : kv;
                 const uint32_t boff = (uint32_t)((kvt + (int64_t)jj * p.ldb) * (int64_t)sizeof(T));
-                u4v v = ld16(rs, boff, p.b_vec);
-#pragma unroll
-                for (int e = 0; e < VR; ++e)
-                    if (k0 + kv + e >= Kr)
-#pragma unroll
-                        for (int d = 0; d < DW; ++d) v[e * DW + d] = 0u;
-                rb[s] = v;
+                rb[s] = ld16<VEC>(rs, boff);
             }
         }
     };
 
-    auto store_tiles = [&](int buf) {
+    // Registers of K tile kt -> LDS buffer buf; entries with k >= K become
+    // zero (only the last, ragged K tile has any: a uniform test first).
+    auto store_tiles = [&](int buf, int kt) {
+        const int64_t k0 = (int64_t)kt * KT;
+        const int64_t k0t = CPLX ? k0 / 2 : k0;
+        const bool ragged = k0 + KT > Kr;  // wave-uniform
 #pragma unroll
         for (int s = 0; s < A_PASSES; ++s) {
             const int flat = s * 256 + tid;
             const int kk = flat / A_TPC;
             const int rr = flat - kk * A_TPC;
-            *reinterpret_cast<u4v *>(&As[buf][kk][rr * AU]) = ra[s];
+            u4v v = ra[s];
+            if (ragged && k0t + kk >= p.K) v = u4v{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u4v *>(&As[buf][kk][rr * AU]) = v;
         }
 #pragma unroll
         for (int s = 0; s < B_PASSES; ++s) {
             const int flat = s * 256 + tid;
             const int jj = flat / B_TPC;
             const int kv = (flat - jj * B_TPC) * VR;
-            *reinterpret_cast<u4v *>(&Bs[buf][jj][kv]) = rb[s];
+            u4v v = rb[s];
+            if (ragged) {
+#pragma unroll
+                for (int e = 0; e < VR; ++e)
+                    if (k0 + kv + e >= Kr)
+#pragma unroll
+                        for (int d = 0; d < DW; ++d) v[e * DW + d] = 0u;
+            }
+            *reinterpret_cast<u4v *>(&Bs[buf][jj][kv]) = v;
         }
     };
 
@@ -337,7 +350,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
 
     if (nkt > 0) {
         load_tiles(0);
-        store_tiles(0);
+        store_tiles(0, 0);
         __syncthreads();
         for (int kt = 0; kt < nkt; ++kt) {
             const int buf = kt & 1;
@@ -380,7 +393,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
                         for (int b = 0; b < FN; ++b) acc[a][b] = Tr::mfma(af[a][e], bf[b][e], acc[a][b]);
             }
             if (kt + 1 < nkt) {
-                store_tiles(buf ^ 1);
+                store_tiles(buf ^ 1, kt + 1);
                 __syncthreads();
             }
         }
@@ -492,10 +505,15 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
     if (tM * tN > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     p.tilesM = (int)tM;
     p.tilesN = (int)tN;
-    if (g.a_lower)
-        hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, true>), dim3((unsigned)(tM * tN)), dim3(256), 0, st, p);
-    else
-        hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, false>), dim3((unsigned)(tM * tN)), dim3(256), 0, st, p);
+    const dim3 grid((unsigned)(tM * tN));
+    const bool vec = p.a_vec && p.b_vec;
+    if (g.a_lower) {
+        if (vec) hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, true, true>), grid, dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, true, false>), grid, dim3(256), 0, st, p);
+    } else {
+        if (vec) hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, false, true>), grid, dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, false, false>), grid, dim3(256), 0, st, p);
+    }
     return hipGetLastError();
 }
 
