@@ -257,7 +257,7 @@ def main():
 
     roofline = {
         "bound": "mfma",
-        "kernel": "update_gemm_f64 (gemm_kernel<double,128,128,16,false>)",
+        "kernel": "update_gemm_f64 (gemm_kernel<double,128,64,16>; 64x64 for the last small updates)",
         "achieved": upd.get("tflops"),
         "peak": PEAK["fp64_mfma_tflops"],
         "unit": "TFLOP/s",

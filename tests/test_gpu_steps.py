@@ -97,8 +97,9 @@ def test_gemm_ragged_shapes(T, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
 def test_gemm_large_tile_path(T, dtype):
-    """Enough 128 x 128 tiles (>= 512) to take the large macro tile, with a
-    ragged K tile and odd leading dimensions (unaligned 16-byte loads)."""
+    """Enough tiles (>= 1024) to take the large macro tile (fp64 128 x 64,
+    complex 64 x 128), with a ragged K tile and odd leading dimensions
+    (unaligned 16-byte loads)."""
     M = 1450 if dtype == "c64" else 2900
     gemm_case(T, dtype, M, 2900, 45, 1.0, -1.0, seed=3)
     gemm_case(T, dtype, M, 2900, 40, 0.0, 1.0, seed=4, ldpad=3)

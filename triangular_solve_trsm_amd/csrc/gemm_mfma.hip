@@ -517,13 +517,23 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Macro tile by launch size: 128 x 128 when that gives at least two tiles
-// per CU (256 CUs), else 64 x 64.
+// Macro tile, from timings on MI355X of the update and solve sequences of
+// blocked solves (fp32 4096^2, fp64 1024^2 .. 8192^2, complex 8192 x 2048):
+// 64 x 64 for the triangular products, for fp32 and for small launches; for
+// large updates 128 x 64 (fp64) or 64 x 128 (complex, whose 64 real rows are
+// 32 complex rows) once that shape gives at least 1024 tiles, four per CU.
+// A 128 x 128 tile needs ~250 VGPRs and 70 KB of LDS, which leaves too few
+// waves per CU to cover its loads; it lost on every shape measured.
 template <typename T, int KT>
 hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
-    const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
-    const int64_t big = ((Mr + 127) / 128) * ((g.N + 127) / 128);
-    if (big >= 512) return launch_tile<T, 128, 128, KT>(g, st);
+    if (!g.a_lower) {
+        const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
+        if constexpr (GemmTraits<T>::kCplx) {
+            if (((Mr + 63) / 64) * ((g.N + 127) / 128) >= 1024) return launch_tile<T, 64, 128, KT>(g, st);
+        } else if constexpr (sizeof(T) == 8) {
+            if (((Mr + 127) / 128) * ((g.N + 63) / 64) >= 1024) return launch_tile<T, 128, 64, KT>(g, st);
+        }
+    }
     return launch_tile<T, 64, 64, KT>(g, st);
 }
 
