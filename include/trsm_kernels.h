@@ -25,6 +25,11 @@ extern "C" {
  * W + t*ib*ib, column-major with leading dimension ib, lower triangular with
  * explicit zeros above the diagonal; the last block covers m - t*ib rows and
  * columns (entries outside it are not written).
+ * The 64 x 64 diagonal blocks are inverted by substitution (section 4.3.1)
+ * and combined into ib x ib inverses by recursive doubling on the matrix
+ * cores; for ib > 64 the scratch of that step comes from the library's
+ * per-(device, stream) workspace (TRSM_STATUS_ALLOC_FAILED if it cannot
+ * grow).
  * ib in {64, 128, 256, 512}; m >= 0.
  */
 trsm_status_t trsm_kernel_diag_inv(trsm_dtype_t dtype, int ib, int64_t m, const void *A,

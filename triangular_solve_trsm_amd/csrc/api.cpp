@@ -200,7 +200,11 @@ trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void
     const int64_t nb = (m + ib - 1) / ib;
     size_t wbytes = (size_t)nb * ib * ib * es;
     wbytes = (wbytes + 255) & ~(size_t)255;
-    const size_t pbytes = (size_t)ib * n * es;
+    // the panel buffer P doubles as the inversion's scratch (P is first
+    // written after the inversion, in the same stream)
+    size_t pbytes = (size_t)ib * n * es;
+    const size_t tbytes = (size_t)diag_inv_tmp_elems(ib, m) * es;
+    if (tbytes > pbytes) pbytes = tbytes;
     void *ws = nullptr;
     trsm_status_t s = get_workspace(dev, st, wbytes + pbytes, &ws);
     if (s != TRSM_STATUS_SUCCESS) return s;
@@ -215,7 +219,7 @@ trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void
     hipError_t e;
     {
         LaunchTimer t(TRSM_KERNEL_DIAG_INV, dt, m, ib, 0, nb, st);
-        e = diag_inv_launch(dt, ib, m, A, lda, W, st);
+        e = diag_inv_launch(dt, ib, m, A, lda, W, P, st);
     }
     if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
     const int64_t bs0 = m < ib ? m : ib;
@@ -370,8 +374,14 @@ trsm_status_t trsm_kernel_diag_inv(trsm_dtype_t dtype, int ib, int64_t m, const 
         int dev = 0;
         trsm_status_t s = check_device(&dev);
         if (s != TRSM_STATUS_SUCCESS) return s;
+        void *tmp = nullptr;
+        const size_t tbytes = (size_t)diag_inv_tmp_elems(ib, m) * dtype_size(dtype);
+        if (tbytes > 0) {
+            s = get_workspace(dev, stream, tbytes, &tmp);
+            if (s != TRSM_STATUS_SUCCESS) return s;
+        }
         LaunchTimer t(TRSM_KERNEL_DIAG_INV, dtype, m, ib, 0, (m + ib - 1) / ib, stream);
-        return hip_status(diag_inv_launch(dtype, ib, m, A, lda, W, stream));
+        return hip_status(diag_inv_launch(dtype, ib, m, A, lda, W, tmp, stream));
     } catch (...) {
         return TRSM_STATUS_HIP_ERROR;
     }

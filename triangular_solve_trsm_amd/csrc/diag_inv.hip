@@ -9,23 +9,38 @@
 // on-chip footprint grows with ib and not with ib^2; the next column is
 // fetched while the current one is used (double buffering).
 //
-// gfx950 mapping (one wavefront per workgroup, no barriers):
-//   * task (t, c) computes columns [c*P, c*P + P) of W_t = D_t^{-1}; the
-//     tasks of one block run on one XCD, sharing its L2;
-//   * lane l owns rows l*R .. l*R + R - 1 (R = ib/64) of those P columns, as
-//     R x P values in VGPRs (the identity tile is generated in registers);
+// On gfx950 the substitution is a serial chain as long as the block: at
+// ib = 512 the wave that owns the first columns runs 512 dependent steps
+// while the chip holds few enough tasks to leave most SIMDs idle.  So the
+// substitution is used at 64 x 64 only, and the rest is built by recursive
+// doubling on the matrix cores:
+//
+//   1. every 64 x 64 diagonal block is inverted by the column-streamed
+//      substitution below, written straight into its place in W;
+//   2. for b = 64, 128, .., ib/2 each pair of neighbouring inverted b x b
+//      blocks [W11 0; . W22] of one ib block becomes the inverse of the
+//      2b x 2b block [L11 0; L21 L22] through its lower-left block
+//      X21 = -W22 L21 W11, two batched GEMMs per level (W22 L21 with the
+//      triangular A path, then -(W22 L21) W11).
+//
+// Substitution kernel, gfx950 mapping (one wavefront per workgroup, no
+// barriers):
+//   * task (t, c) computes columns [c*P, c*P + P) of the inverse of 64R x 64R
+//     diagonal block t; the tasks of one block run on one XCD, sharing its L2;
+//   * lane l owns rows l*R .. l*R + R - 1 of those P columns, as R x P values
+//     in VGPRs (the identity tile is generated in registers);
 //   * step k (k = c*P .. bs-1): the lane owning row k scales its row by the
 //     reciprocal of d_kk; the P solved values are broadcast to the wave with
 //     v_readlane (SGPR operands of the following FMAs); every lane subtracts
 //     d_ik * x_k from its rows i > k;
 //   * column k of D_t is read straight into VGPRs, each lane its own rows.
 //     Figure 7 alternates two column buffers (compute one, fetch the next);
-//     here the buffers are a ring of several columns in registers (the CDNA4
-//     register file is 512 KB per CU), because one column ahead is far less
-//     than the memory latency at a few hundred cycles per step.  LDS is not
-//     used at all, so the footprint stays O(ib) per wavefront.
-// Rows above the diagonal are written as explicit zeros, which the triangular
-// GEMM of the solve phase relies on.
+//     here the buffers are a ring of several columns in registers, because
+//     one column ahead is far less than the memory latency.  LDS is not used.
+// Everything above the diagonal of each ib x ib block of W is written as an
+// explicit zero (the substitution tile's own upper part, and the columns
+// right of it inside the ib block): the doubling step reads W11 as a full
+// operand, and the triangular GEMM of the solve phase relies on the zeros.
 #include "buffer_ops.h"
 #include "scalar_ops.h"
 
@@ -49,14 +64,6 @@ __device__ __forceinline__ cplx bcast(cplx v, int src) {
 
 template <typename T> constexpr int words() { return sizeof(T) / 4; }
 
-// Columns per wavefront: keep R x P values of T within 128 VGPRs.
-template <typename T, int R>
-constexpr int panel_cols() {
-    constexpr int ib = 64 * R;
-    constexpr int p = 128 / (R * words<T>());
-    return p < ib ? p : ib;
-}
-
 // Columns of D in flight: a ring of DP columns (R values of T per lane each)
 // within 128 VGPRs, between 2 and 16.  At a few hundred cycles per step,
 // several columns ahead cover the memory latency that one column ahead left
@@ -67,13 +74,16 @@ constexpr int ring_cols() {
     return d < 2 ? 2 : (d > 16 ? 16 : d);
 }
 
-template <typename T, int R, bool VEC>
+// Diagonal blocks of 64R x 64R, P columns per task.  Block t (rows
+// [t*64R, ..)) is written at its place inside the ldw x ldw blocks of W
+// (ldw a multiple of 64R): parent block t*64R / ldw, at rows and columns
+// (t*64R) % ldw of it.
+template <typename T, int R, int P, bool VEC>
 __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__restrict__ A,
-                                                      int64_t lda, T *__restrict__ W,
+                                                      int64_t lda, T *__restrict__ W, int ldw,
                                                       int npanels) {
     using E = Elem<T>;
     constexpr int IB = 64 * R;
-    constexpr int P = panel_cols<T, R>();
     constexpr int DP = ring_cols<T, R>();
     constexpr int U = DP > R ? DP : R;  // steps per unrolled group (multiple of both)
     // Workgroups go round-robin to the 8 XCDs (workgroup b on XCD b % 8);
@@ -88,15 +98,25 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
     const int lane = threadIdx.x;
     const int64_t base = (int64_t)t * IB;
     const int bs = (int)((m - base) < IB ? (m - base) : IB);
+    const int row0 = lane * R;  // this lane's rows row0 .. row0 + R - 1
+    const int64_t tp = base / ldw;
+    const int lo = (int)(base - tp * ldw);
+    const int bsp = (int)((m - tp * ldw) < ldw ? (m - tp * ldw) : ldw);
+    T *__restrict__ Wt = W + tp * (int64_t)ldw * ldw + (int64_t)lo * (ldw + 1);
+    // zeros in this block's rows right of it inside the parent block, the
+    // columns shared out over the panel tasks
+    for (int j = IB + c; lo + j < bsp; j += npanels) {
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+            if (row0 + rr < bs) Wt[row0 + rr + (int64_t)j * ldw] = E::zero();
+    }
     const int j0 = c * P;
     if (j0 >= bs) return;
-    T *__restrict__ Wt = W + (int64_t)t * IB * IB;
     // D(i, k) at element i + k * lda from here; reads past A's last element
     // return zero (they only reach rows and columns >= bs, which are unused).
     const int64_t doff = base + base * lda;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(A + doff, ((m - 1) + (m - 1) * lda + 1 - doff) * (int64_t)sizeof(T));
-    const int row0 = lane * R;  // this lane's rows row0 .. row0 + R - 1
     auto col_off = [&](int k) -> uint32_t {
         return (uint32_t)(((int64_t)row0 + (int64_t)k * lda) * (int64_t)sizeof(T));
     };
@@ -156,55 +176,162 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
             const int i = row0 + rr;
-            if (i < bs) Wt[i + (int64_t)j * IB] = x[rr][jj];
+            if (i < bs) Wt[i + (int64_t)j * ldw] = x[rr][jj];
         }
     }
 }
 
-template <typename T, int R>
-hipError_t launch_r(int64_t m, const void *A, int64_t lda, void *W, hipStream_t st) {
+template <typename T, int R, int P>
+hipError_t launch_r(int64_t m, const void *A, int64_t lda, void *W, int ldw, hipStream_t st) {
     constexpr int IB = 64 * R;
-    constexpr int P = panel_cols<T, R>();
     const int64_t nb = (m + IB - 1) / IB;
     const int npanels = (IB + P - 1) / P;
     const int64_t total = nb * npanels;
     if (total <= 0) return hipSuccess;
     if (total > 0x7fffffffLL - 8) return hipErrorInvalidConfiguration;
+    if (ldw % IB != 0) return hipErrorInvalidValue;
     const int64_t grid = 8 * ((total + 7) / 8);  // whole rounds over the 8 XCDs
     // 32-bit buffer offsets reach one diagonal block: IB columns of lda
     if ((int64_t)sizeof(T) * (lda + 1) * IB > 0x7fffffffLL) return hipErrorInvalidValue;
     const int vec = (reinterpret_cast<uintptr_t>(A) % 16 == 0) &&
                     ((int64_t)sizeof(T) * lda) % 16 == 0;
     if (vec)
-        hipLaunchKernelGGL((diag_inv_kernel<T, R, true>), dim3((unsigned)grid), dim3(64), 0, st, m,
-                           static_cast<const T *>(A), lda, static_cast<T *>(W), npanels);
+        hipLaunchKernelGGL((diag_inv_kernel<T, R, P, true>), dim3((unsigned)grid), dim3(64), 0, st, m,
+                           static_cast<const T *>(A), lda, static_cast<T *>(W), ldw, npanels);
     else
-        hipLaunchKernelGGL((diag_inv_kernel<T, R, false>), dim3((unsigned)grid), dim3(64), 0, st, m,
-                           static_cast<const T *>(A), lda, static_cast<T *>(W), npanels);
+        hipLaunchKernelGGL((diag_inv_kernel<T, R, P, false>), dim3((unsigned)grid), dim3(64), 0, st, m,
+                           static_cast<const T *>(A), lda, static_cast<T *>(W), ldw, npanels);
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_t(int ib, int64_t m, const void *A, int64_t lda, void *W, hipStream_t st) {
-    switch (ib) {
-        case 64: return launch_r<T, 1>(m, A, lda, W, st);
-        case 128: return launch_r<T, 2>(m, A, lda, W, st);
-        case 256: return launch_r<T, 4>(m, A, lda, W, st);
-        case 512: return launch_r<T, 8>(m, A, lda, W, st);
+// 64 x 64 substitution with 16 columns per task: four tasks per block keep
+// the chain short (64 steps of 16 columns) and give the chip m/16 waves.
+constexpr int kBase = 64;
+constexpr int kBaseCols = 16;
+
+hipError_t launch_base(int dtype, int64_t m, const void *A, int64_t lda, void *W, int ldw,
+                       hipStream_t st) {
+    switch (dtype) {
+        case R32F: return launch_r<float, 1, kBaseCols>(m, A, lda, W, ldw, st);
+        case R64F: return launch_r<double, 1, kBaseCols>(m, A, lda, W, ldw, st);
+        case C64F: return launch_r<cplx, 1, kBaseCols>(m, A, lda, W, ldw, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+int64_t diag_inv_tmp_elems(int ib, int64_t m) {
+    if (ib <= kBase || m <= 0) return 0;
+    const int64_t nb = (m + ib - 1) / ib;
+    return nb * (int64_t)ib * (ib / 2) / 2;  // the largest level, b = ib/2
+}
+
 hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t lda, void *W,
-                           hipStream_t stream) {
-    switch (dtype) {
-        case R32F: return launch_t<float>(ib, m, A, lda, W, stream);
-        case R64F: return launch_t<double>(ib, m, A, lda, W, stream);
-        case C64F: return launch_t<cplx>(ib, m, A, lda, W, stream);
-        default: return hipErrorInvalidValue;
+                           void *tmp, hipStream_t stream) {
+    if (ib != 64 && ib != 128 && ib != 256 && ib != 512) return hipErrorInvalidValue;
+    if (m <= 0) return hipSuccess;
+    hipError_t e = launch_base(dtype, m, A, lda, W, ib, stream);
+    if (e != hipSuccess || ib <= kBase) return e;
+    if (tmp == nullptr) return hipErrorInvalidValue;
+    const int64_t es = (int64_t)dtype_size(dtype);
+    const int64_t nb = (m + ib - 1) / ib;
+    const int64_t bsl = m - (nb - 1) * ib;  // rows of the last ib block
+    const char *Ab = static_cast<const char *>(A);
+    char *Wb = static_cast<char *>(W);
+    char *Tb = static_cast<char *>(tmp);
+    const Scalar zero{0.0, 0.0}, one{1.0, 0.0}, minus_one{-1.0, 0.0};
+    for (int64_t b = kBase; b < ib; b *= 2) {
+        // pairs of b x b blocks: pair (zo, zi) starts at row/column
+        // o = zo*ib + zi*2b; W11 at (o, o), W22 and L22 at (o+b, o+b),
+        // L21 and X21 at (o+b, o); the product W22 L21 goes to tmp
+        // (b x b, ld b, pair after pair)
+        const int64_t pp = ib / (2 * b);
+        const int64_t full_last = bsl / (2 * b);
+        const int64_t nfull = (nb - 1) * pp + full_last;
+        if (nfull > 0) {
+            GemmDesc g1{};  // tmp = W22 * L21
+            g1.M = g1.N = g1.K = b;
+            g1.A = Wb + b * (1 + ib) * es;
+            g1.lda = ib;
+            g1.a_lower = 1;
+            g1.Bm = Ab + b * es;
+            g1.ldb = lda;
+            g1.D = Tb;
+            g1.ldd = b;
+            g1.ldc = b;
+            g1.ldd2 = b;
+            g1.beta = zero;
+            g1.gamma = one;
+            g1.batch = nfull;
+            g1.binner = pp;
+            g1.sAo = (int64_t)ib * ib;
+            g1.sAi = 2 * b * (1 + ib);
+            g1.sBo = (int64_t)ib * (1 + lda);
+            g1.sBi = 2 * b * (1 + lda);
+            g1.sDo = pp * b * b;
+            g1.sDi = b * b;
+            if ((e = gemm_launch(dtype, g1, stream)) != hipSuccess) return e;
+            GemmDesc g2{};  // X21 = -tmp * W11
+            g2.M = g2.N = g2.K = b;
+            g2.A = Tb;
+            g2.lda = b;
+            g2.Bm = Wb;
+            g2.ldb = ib;
+            g2.D = Wb + b * es;
+            g2.ldd = ib;
+            g2.ldc = ib;
+            g2.ldd2 = ib;
+            g2.beta = zero;
+            g2.gamma = minus_one;
+            g2.batch = nfull;
+            g2.binner = pp;
+            g2.sAo = pp * b * b;
+            g2.sAi = b * b;
+            g2.sBo = (int64_t)ib * ib;
+            g2.sBi = 2 * b * (1 + ib);
+            g2.sDo = (int64_t)ib * ib;
+            g2.sDi = 2 * b * (1 + ib);
+            if ((e = gemm_launch(dtype, g2, stream)) != hipSuccess) return e;
+        }
+        // a last pair whose second block is cut short by the end of L
+        const int64_t o = 2 * b * full_last;
+        const int64_t r = bsl - o - b;  // rows of its second block, < b
+        if (r > 0) {
+            const char *Wt = Wb + (nb - 1) * ib * ib * es;
+            const char *At = Ab + (nb - 1) * ib * (1 + lda) * es;
+            GemmDesc g1{};
+            g1.M = g1.K = r;
+            g1.N = b;
+            g1.A = Wt + (o + b) * (1 + ib) * es;
+            g1.lda = ib;
+            g1.a_lower = 1;
+            g1.Bm = At + ((o + b) + o * lda) * es;
+            g1.ldb = lda;
+            g1.D = Tb;
+            g1.ldd = b;
+            g1.ldc = b;
+            g1.ldd2 = b;
+            g1.beta = zero;
+            g1.gamma = one;
+            if ((e = gemm_launch(dtype, g1, stream)) != hipSuccess) return e;
+            GemmDesc g2{};
+            g2.M = r;
+            g2.N = g2.K = b;
+            g2.A = Tb;
+            g2.lda = b;
+            g2.Bm = Wt + o * (1 + ib) * es;
+            g2.ldb = ib;
+            g2.D = const_cast<char *>(Wt) + ((o + b) + o * ib) * es;
+            g2.ldd = ib;
+            g2.ldc = ib;
+            g2.ldd2 = ib;
+            g2.beta = zero;
+            g2.gamma = minus_one;
+            if ((e = gemm_launch(dtype, g2, stream)) != hipSuccess) return e;
+        }
     }
+    return hipSuccess;
 }
 
 }  // namespace trsm

@@ -112,6 +112,8 @@ struct GemmParams {
     int a_vec, b_vec;        // 16-byte aligned operand loads
     int c_vec, d_vec, d2_vec;  // 16-byte aligned C / D / D2 columns
     int tilesM, tilesN;
+    int binner;  // batched launches (gridDim.y problems): see GemmDesc
+    int64_t sAo, sAi, sBo, sBi, sCo, sCi, sDo, sDi;
 };
 
 // Workgroup -> tile: consecutive workgroups go round-robin to the 8 XCDs, so
@@ -206,6 +208,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     const int q = lane >> 4;
 
     if (blockIdx.x >= (unsigned)(p.tilesM * p.tilesN)) return;
+    if (gridDim.y > 1) {  // problem blockIdx.y of a batch (uniform)
+        const int zo = (int)blockIdx.y / p.binner;
+        const int zi = (int)blockIdx.y - zo * p.binner;
+        p.A += zo * p.sAo + zi * p.sAi;
+        p.Bm += zo * p.sBo + zi * p.sBi;
+        p.C += zo * p.sCo + zi * p.sCi;
+        p.D += zo * p.sDo + zi * p.sDi;
+        p.D2 += zo * p.sDo + zi * p.sDi;
+    }
     int tm, tn;
     map_tile(blockIdx.x, p.tilesM, p.tilesN, tm, tn);
 
@@ -505,7 +516,21 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
     if (tM * tN > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     p.tilesM = (int)tM;
     p.tilesN = (int)tN;
-    const dim3 grid((unsigned)(tM * tN));
+    const int64_t nz = g.batch > 1 ? g.batch : 1;
+    if (nz > 65535) return hipErrorInvalidConfiguration;
+    p.binner = nz > 1 ? (int)g.binner : 1;
+    p.sAo = g.sAo; p.sAi = g.sAi; p.sBo = g.sBo; p.sBi = g.sBi;
+    p.sCo = g.sCo; p.sCi = g.sCi; p.sDo = g.sDo; p.sDi = g.sDi;
+    if (nz > 1) {
+        if (g.split != 0 || g.binner < 1 || g.binner > nz) return hipErrorInvalidValue;
+        // every problem's operands keep the alignment of the first
+        const auto al = [&](int64_t o, int64_t i) { return (o * (int64_t)es) % 16 == 0 && (i * (int64_t)es) % 16 == 0; };
+        if (!al(g.sAo, g.sAi)) p.a_vec = 0;
+        if (!al(g.sBo, g.sBi)) p.b_vec = 0;
+        if (!al(g.sCo, g.sCi)) p.c_vec = 0;
+        if (!al(g.sDo, g.sDi)) p.d_vec = p.d2_vec = 0;
+    }
+    const dim3 grid((unsigned)(tM * tN), (unsigned)nz);
     const bool vec = p.a_vec && p.b_vec;
     if (g.a_lower) {
         if (vec) hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, true, true>), grid, dim3(256), 0, st, p);
@@ -526,7 +551,7 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
 // waves per CU to cover its loads; it lost on every shape measured.
 template <typename T, int KT>
 hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
-    if (!g.a_lower) {
+    if (!g.a_lower && g.batch <= 1) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
         if constexpr (GemmTraits<T>::kCplx) {
             if (((Mr + 63) / 64) * ((g.N + 127) / 128) >= 1024) return launch_tile<T, 64, 128, KT>(g, st);

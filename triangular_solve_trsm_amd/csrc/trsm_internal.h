@@ -39,9 +39,12 @@ hipError_t small_mfma_launch(int dtype, int m, int64_t n, Scalar alpha, const vo
 
 // ---- kernel (b1): inversion of every ib x ib diagonal block ---------------
 // W receives ceil(m/ib) blocks, block t at W + t*ib*ib (column-major, ld ib),
-// each lower triangular with explicit zeros above the diagonal.
+// each lower triangular with explicit zeros above the diagonal.  tmp holds
+// diag_inv_tmp_elems(ib, m) elements of scratch (may be null when that is 0);
+// it must not overlap W or A.
+int64_t diag_inv_tmp_elems(int ib, int64_t m);
 hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t lda,
-                           void *W, hipStream_t stream);
+                           void *W, void *tmp, hipStream_t stream);
 
 // ---- kernels (b2, b3): MFMA GEMM -----------------------------------------
 //   D = beta * C + gamma * (A * Bm)
@@ -50,6 +53,10 @@ hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t 
 // C may alias D (in place).  beta == 0 means C is not read (may be null).
 // a_lower != 0: A is lower triangular (explicit zeros above the diagonal);
 // K-tiles to the right of a row tile's diagonal are skipped (requires M == K).
+// batch > 1: `batch` independent problems of the same shape; problem
+// z = zo * binner + zi (0 <= zi < binner) finds its operands at element
+// offsets zo * s?o + zi * s?i from the pointers (split must be 0).  A
+// value-initialised descriptor (batch 0) is a single problem.
 struct GemmDesc {
     int64_t M, N, K;
     const void *A;
@@ -65,6 +72,8 @@ struct GemmDesc {
     int64_t split;
     Scalar beta, gamma;
     int a_lower;
+    int64_t batch, binner;
+    int64_t sAo, sAi, sBo, sBi, sCo, sCi, sDo, sDi;
 };
 hipError_t gemm_launch(int dtype, const GemmDesc &g, hipStream_t stream);
 
