@@ -15,8 +15,8 @@
 //
 // gfx950 mapping:
 //   * 256 threads = 2 x 2 wavefronts on a macro tile of MT x NT real rows x
-//     columns (128 x 128, or 64 x 64 when a launch has too few tiles to give
-//     every CU two of them); each wave owns (MT/2) x (NT/2) as 16 x 16 tiles
+//     columns (64 x 32 up to 128 x 64 by launch shape, see launch_sized);
+//     each wave owns (MT/2) x (NT/2) as 16 x 16 tiles
 //     of v_mfma_f64_16x16x4f64 (fp64, complex fp64) or
 //     v_mfma_f32_16x16x4f32 (fp32: true fp32 products, no reduced-precision
 //     splitting);
@@ -45,6 +45,9 @@
 //     expanded on the fly from the complex tile in LDS, and the real rows are
 //     ordered so that each lane holds whole complex results.  This is exactly
 //     the 4 real products per complex product (no 3M trick);
+//   * with a triangular A the work of row tile i grows with i, so each
+//     workgroup computes row tiles i and tilesM-1-i of one column tile, one
+//     after the other: every workgroup gets the same amount of work;
 //   * tiles are mapped so that each XCD (8 per chip, each with its own L2)
 //     works on a band of 8 column tiles at a time, and the workgroups of one
 //     XCD cover roughly 8 x 8 tiles, sharing the A and Bm panels in its L2.
@@ -207,258 +210,268 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     const int c16 = lane & 15;
     const int q = lane >> 4;
 
-    if (blockIdx.x >= (unsigned)(p.tilesM * p.tilesN)) return;
-    if (gridDim.y > 1) {  // problem blockIdx.y of a batch (uniform)
-        const int zo = (int)blockIdx.y / p.binner;
-        const int zi = (int)blockIdx.y - zo * p.binner;
-        p.A += zo * p.sAo + zi * p.sAi;
-        p.Bm += zo * p.sBo + zi * p.sBi;
-        p.C += zo * p.sCo + zi * p.sCi;
-        p.D += zo * p.sDo + zi * p.sDi;
-        p.D2 += zo * p.sDo + zi * p.sDi;
-    }
-    int tm, tn;
-    map_tile(blockIdx.x, p.tilesM, p.tilesN, tm, tn);
+    // triangular A: workgroup w takes row tiles i and tilesM-1-i of one
+    // column tile (their K ranges sum to the same length for every i)
+    const int rowsM = TRI ? (p.tilesM + 1) / 2 : p.tilesM;
+    if (blockIdx.x >= (unsigned)(rowsM * p.tilesN)) return;
+    // Operands of problem blockIdx.y of a batch.  Kept in locals: `p` is
+    // never written, so its fields stay scalar (kernel-argument) loads.
+    const int zo = (int)blockIdx.y / p.binner;
+    const int zi = (int)blockIdx.y - zo * p.binner;
+    const T *__restrict__ pA = p.A + (zo * p.sAo + zi * p.sAi);
+    const T *__restrict__ pB = p.Bm + (zo * p.sBo + zi * p.sBi);
+    const T *__restrict__ pC = p.C + (zo * p.sCo + zi * p.sCi);
+    T *__restrict__ pD = p.D + (zo * p.sDo + zi * p.sDi);
+    T *__restrict__ pD2 = p.D2 + (zo * p.sDo + zi * p.sDi);
+    int tm0, tn;
+    map_tile(blockIdx.x, rowsM, p.tilesN, tm0, tn);
 
-    const int64_t Kr = CPLX ? 2 * p.K : p.K;  // real K
-    const int64_t i0 = (int64_t)tm * MT;      // real row offset of the tile
-    const int64_t j0 = (int64_t)tn * NT;
-    const int64_t i0t = CPLX ? i0 / 2 : i0;
-    int64_t kend = Kr;
-    if (TRI) {
-        const int64_t lim = i0 + MT;  // real rows; K has the same (real) scale
-        kend = lim < Kr ? lim : Kr;
-    }
-    const int nkt = (int)((kend + KT - 1) / KT);
+    // one pass per row tile: tm0, then (triangular A) its partner
+    const int tm1 = p.tilesM - 1 - tm0;
+    const int npass = (TRI && tm1 != tm0) ? 2 : 1;
+    for (int pass = 0; pass < npass; ++pass) {
+        const int tm = pass == 0 ? tm0 : tm1;
+        if (pass > 0) __syncthreads();  // the LDS buffers are reused
+        const int64_t Kr = CPLX ? 2 * p.K : p.K;  // real K
+        const int64_t i0 = (int64_t)tm * MT;      // real row offset of the tile
+        const int64_t j0 = (int64_t)tn * NT;
+        const int64_t i0t = CPLX ? i0 / 2 : i0;
+        int64_t kend = Kr;
+        if (TRI) {
+            const int64_t lim = i0 + MT;  // real rows; K has the same (real) scale
+            kend = lim < Kr ? lim : Kr;
+        }
+        const int nkt = (int)((kend + KT - 1) / KT);
 
-    // ---- accumulators start at sc * C ----------------------------------
-    Acc acc[FM][FN];
-    if (p.has_c) {
-        if constexpr (CPLX) {
-            const cplx sc{p.sc.re, p.sc.im};
+        // ---- accumulators start at sc * C ----------------------------------
+        Acc acc[FM][FN];
+        if (p.has_c) {
+            if constexpr (CPLX) {
+                const cplx sc{p.sc.re, p.sc.im};
 #pragma unroll
-            for (int a = 0; a < FM; ++a) {
-                const int64_t cb = (i0 + wm * WM + a * 16) / 2 + 2 * q;  // complex rows cb, cb+1
+                for (int a = 0; a < FM; ++a) {
+                    const int64_t cb = (i0 + wm * WM + a * 16) / 2 + 2 * q;  // complex rows cb, cb+1
 #pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const int64_t j = j0 + wn * WN + b * 16 + c16;
-                    cplx z0{0.0, 0.0}, z1{0.0, 0.0};
-                    if (j < p.N) {
-                        if (cb < p.M) z0 = Elem<cplx>::mul(sc, p.C[cb + j * p.ldc]);
-                        if (cb + 1 < p.M) z1 = Elem<cplx>::mul(sc, p.C[cb + 1 + j * p.ldc]);
+                    for (int b = 0; b < FN; ++b) {
+                        const int64_t j = j0 + wn * WN + b * 16 + c16;
+                        cplx z0{0.0, 0.0}, z1{0.0, 0.0};
+                        if (j < p.N) {
+                            if (cb < p.M) z0 = Elem<cplx>::mul(sc, pC[cb + j * p.ldc]);
+                            if (cb + 1 < p.M) z1 = Elem<cplx>::mul(sc, pC[cb + 1 + j * p.ldc]);
+                        }
+                        acc[a][b] = Acc{z0.re, z0.im, z1.re, z1.im};
                     }
-                    acc[a][b] = Acc{z0.re, z0.im, z1.re, z1.im};
+                }
+            } else {
+                const R sc = (R)p.sc.re;
+#pragma unroll
+                for (int a = 0; a < FM; ++a) {
+                    const int64_t r = i0 + wm * WM + a * 16 + 4 * q;
+#pragma unroll
+                    for (int b = 0; b < FN; ++b) {
+                        const int64_t j = j0 + wn * WN + b * 16 + c16;
+                        R cv[4] = {R(0), R(0), R(0), R(0)};
+                        if (j < p.N) load_rows4<R>(pC, p.ldc, p.M, r, j, p.c_vec, cv);
+                        acc[a][b] = Acc{sc * cv[0], sc * cv[1], sc * cv[2], sc * cv[3]};
+                    }
                 }
             }
         } else {
-            const R sc = (R)p.sc.re;
 #pragma unroll
-            for (int a = 0; a < FM; ++a) {
-                const int64_t r = i0 + wm * WM + a * 16 + 4 * q;
+            for (int a = 0; a < FM; ++a)
 #pragma unroll
-                for (int b = 0; b < FN; ++b) {
-                    const int64_t j = j0 + wn * WN + b * 16 + c16;
-                    R cv[4] = {R(0), R(0), R(0), R(0)};
-                    if (j < p.N) load_rows4<R>(p.C, p.ldc, p.M, r, j, p.c_vec, cv);
-                    acc[a][b] = Acc{sc * cv[0], sc * cv[1], sc * cv[2], sc * cv[3]};
+                for (int b = 0; b < FN; ++b) acc[a][b] = Acc{0, 0, 0, 0};
+        }
+
+        // ---- global -> register staging ------------------------------------
+        constexpr int A_TPC = AR / AU;  // threads per A column
+        constexpr int A_CPP = 256 / A_TPC;
+        constexpr int A_PASSES = AK / A_CPP;
+        static_assert(A_PASSES * A_CPP == AK, "A tile shape");
+        constexpr int B_TPC = KT / VR;  // threads per Bm column (real view)
+        constexpr int B_CPP = 256 / B_TPC;
+        constexpr int B_PASSES = NT / B_CPP;
+        static_assert(B_PASSES * B_CPP == NT, "B tile shape");
+        constexpr int DW = (int)sizeof(R) / 4;  // dwords per real
+
+        u4v ra[A_PASSES];
+        u4v rb[B_PASSES];
+
+        // Loads of K tile kt into registers.  The ragged-K mask is applied when
+        // the registers are written to LDS (store_tiles), not here: a select on
+        // the loaded values would make the compiler wait for the loads right
+        // after issuing them, before the MFMAs they are meant to overlap.
+        auto load_tiles = [&](int kt) {
+            const int64_t k0 = (int64_t)kt * KT;  // real k offset
+            const int64_t k0t = CPLX ? k0 / 2 : k0;
+            {
+                const int64_t off = i0t + k0t * p.lda;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(pA + off, (p.extA - off) * (int64_t)sizeof(T));
+#pragma unroll
+                for (int s = 0; s < A_PASSES; ++s) {
+                    const int flat = s * 256 + tid;
+                    const int kk = flat / A_TPC;
+                    const int rr = flat - kk * A_TPC;
+                    const uint32_t boff = (uint32_t)(((int64_t)rr * AU + (int64_t)kk * p.lda) * (int64_t)sizeof(T));
+                    ra[s] = ld16<VEC>(rs, boff);
                 }
             }
-        }
-    } else {
+            {
+                const int64_t off = k0t + j0 * p.ldb;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(pB + off, (p.extB - off) * (int64_t)sizeof(T));
 #pragma unroll
-        for (int a = 0; a < FM; ++a)
-#pragma unroll
-            for (int b = 0; b < FN; ++b) acc[a][b] = Acc{0, 0, 0, 0};
-    }
+                for (int s = 0; s < B_PASSES; ++s) {
+                    const int flat = s * 256 + tid;
+                    const int jj = flat / B_TPC;
+                    const int kv = (flat - jj * B_TPC) * VR;  // real k inside the tile
+                    const int64_t kvt = CPLX ? kv / 2 : kv;
+                    const uint32_t boff = (uint32_t)((kvt + (int64_t)jj * p.ldb) * (int64_t)sizeof(T));
+                    rb[s] = ld16<VEC>(rs, boff);
+                }
+            }
+        };
 
-    // ---- global -> register staging ------------------------------------
-    constexpr int A_TPC = AR / AU;  // threads per A column
-    constexpr int A_CPP = 256 / A_TPC;
-    constexpr int A_PASSES = AK / A_CPP;
-    static_assert(A_PASSES * A_CPP == AK, "A tile shape");
-    constexpr int B_TPC = KT / VR;  // threads per Bm column (real view)
-    constexpr int B_CPP = 256 / B_TPC;
-    constexpr int B_PASSES = NT / B_CPP;
-    static_assert(B_PASSES * B_CPP == NT, "B tile shape");
-    constexpr int DW = (int)sizeof(R) / 4;  // dwords per real
-
-    u4v ra[A_PASSES];
-    u4v rb[B_PASSES];
-
-    // Loads of K tile kt into registers.  The ragged-K mask is applied when
-    // the registers are written to LDS (store_tiles), not here: a select on
-    // the loaded values would make the compiler wait for the loads right
-    // after issuing them, before the MFMAs they are meant to overlap.
-    auto load_tiles = [&](int kt) {
-        const int64_t k0 = (int64_t)kt * KT;  // real k offset
-        const int64_t k0t = CPLX ? k0 / 2 : k0;
-        {
-            const int64_t off = i0t + k0t * p.lda;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.A + off, (p.extA - off) * (int64_t)sizeof(T));
+        // Registers of K tile kt -> LDS buffer buf; entries with k >= K become
+        // zero (only the last, ragged K tile has any: a uniform test first).
+        auto store_tiles = [&](int buf, int kt) {
+            const int64_t k0 = (int64_t)kt * KT;
+            const int64_t k0t = CPLX ? k0 / 2 : k0;
+            const bool ragged = k0 + KT > Kr;  // wave-uniform
 #pragma unroll
             for (int s = 0; s < A_PASSES; ++s) {
                 const int flat = s * 256 + tid;
                 const int kk = flat / A_TPC;
                 const int rr = flat - kk * A_TPC;
-                const uint32_t boff = (uint32_t)(((int64_t)rr * AU + (int64_t)kk * p.lda) * (int64_t)sizeof(T));
-                ra[s] = ld16<VEC>(rs, boff);
+                u4v v = ra[s];
+                if (ragged && k0t + kk >= p.K) v = u4v{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u4v *>(&As[buf][kk][rr * AU]) = v;
             }
-        }
-        {
-            const int64_t off = k0t + j0 * p.ldb;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.Bm + off, (p.extB - off) * (int64_t)sizeof(T));
 #pragma unroll
             for (int s = 0; s < B_PASSES; ++s) {
                 const int flat = s * 256 + tid;
                 const int jj = flat / B_TPC;
-                const int kv = (flat - jj * B_TPC) * VR;  // real k inside the tile
-                const int64_t kvt = CPLX ? kv / 2 : kv;
-                const uint32_t boff = (uint32_t)((kvt + (int64_t)jj * p.ldb) * (int64_t)sizeof(T));
-                rb[s] = ld16<VEC>(rs, boff);
+                const int kv = (flat - jj * B_TPC) * VR;
+                u4v v = rb[s];
+                if (ragged) {
+#pragma unroll
+                    for (int e = 0; e < VR; ++e)
+                        if (k0 + kv + e >= Kr)
+#pragma unroll
+                            for (int d = 0; d < DW; ++d) v[e * DW + d] = 0u;
+                }
+                *reinterpret_cast<u4v *>(&Bs[buf][jj][kv]) = v;
+            }
+        };
+
+        // Complex A-fragment expansion (lane-fixed part).  Real row t = c16 of a
+        // 16-row block stands for complex row 2(t % 4) + t / 8 of the block's 8,
+        // part (t / 4) % 2; with the f64 result layout (row q + 4v in item v) a
+        // lane then holds complex rows 2q (items 0, 1) and 2q + 1 (items 2, 3).
+        const int a_crow = 2 * (c16 & 3) + (c16 >> 3);
+        const int a_ri = (c16 >> 2) & 1;
+        const int a_row = Tr::a_row(c16);
+
+        if (nkt > 0) {
+            load_tiles(0);
+            store_tiles(0, 0);
+            __syncthreads();
+            for (int kt = 0; kt < nkt; ++kt) {
+                const int buf = kt & 1;
+                if (kt + 1 < nkt) load_tiles(kt + 1);
+#pragma unroll
+                for (int s0 = 0; s0 < KS; s0 += CW) {
+                    const int kb = q * KS + s0;  // real k of this chunk inside the tile
+                    R bf[FN][CW];
+#pragma unroll
+                    for (int b = 0; b < FN; ++b) {
+                        const u4v v = *reinterpret_cast<const u4v *>(&Bs[buf][wn * WN + b * 16 + c16][kb]);
+                        if constexpr (sizeof(R) == 4) {
+                            const f4 fv = __builtin_bit_cast(f4, v);
+#pragma unroll
+                            for (int e = 0; e < CW; ++e) bf[b][e] = fv[e];
+                        } else {
+                            const d2v dv = __builtin_bit_cast(d2v, v);
+                            bf[b][0] = dv[0];
+                            bf[b][1] = dv[1];
+                        }
+                    }
+                    R af[FM][CW];
+#pragma unroll
+                    for (int a = 0; a < FM; ++a) {
+                        if constexpr (CPLX) {
+                            // real k = kb + e: complex k (kb + e) / 2, part e % 2 (kb even)
+                            const cplx z = As[buf][kb >> 1][(wm * WM + a * 16) / 2 + a_crow];
+                            af[a][0] = a_ri ? z.im : z.re;    // k part 0
+                            af[a][1] = a_ri ? z.re : -z.im;   // k part 1
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < CW; ++e) af[a][e] = As[buf][kb + e][wm * WM + a * 16 + a_row];
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < CW; ++e)
+#pragma unroll
+                        for (int a = 0; a < FM; ++a)
+#pragma unroll
+                            for (int b = 0; b < FN; ++b) acc[a][b] = Tr::mfma(af[a][e], bf[b][e], acc[a][b]);
+                }
+                if (kt + 1 < nkt) {
+                    store_tiles(buf ^ 1, kt + 1);
+                    __syncthreads();
+                }
             }
         }
-    };
 
-    // Registers of K tile kt -> LDS buffer buf; entries with k >= K become
-    // zero (only the last, ragged K tile has any: a uniform test first).
-    auto store_tiles = [&](int buf, int kt) {
-        const int64_t k0 = (int64_t)kt * KT;
-        const int64_t k0t = CPLX ? k0 / 2 : k0;
-        const bool ragged = k0 + KT > Kr;  // wave-uniform
+        // ---- epilogue: D = gamma * acc, rows below `split` to D2 --------------
+        if constexpr (CPLX) {
+            const cplx gamma{p.gamma.re, p.gamma.im};
 #pragma unroll
-        for (int s = 0; s < A_PASSES; ++s) {
-            const int flat = s * 256 + tid;
-            const int kk = flat / A_TPC;
-            const int rr = flat - kk * A_TPC;
-            u4v v = ra[s];
-            if (ragged && k0t + kk >= p.K) v = u4v{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u4v *>(&As[buf][kk][rr * AU]) = v;
-        }
-#pragma unroll
-        for (int s = 0; s < B_PASSES; ++s) {
-            const int flat = s * 256 + tid;
-            const int jj = flat / B_TPC;
-            const int kv = (flat - jj * B_TPC) * VR;
-            u4v v = rb[s];
-            if (ragged) {
-#pragma unroll
-                for (int e = 0; e < VR; ++e)
-                    if (k0 + kv + e >= Kr)
-#pragma unroll
-                        for (int d = 0; d < DW; ++d) v[e * DW + d] = 0u;
-            }
-            *reinterpret_cast<u4v *>(&Bs[buf][jj][kv]) = v;
-        }
-    };
-
-    // Complex A-fragment expansion (lane-fixed part).  Real row t = c16 of a
-    // 16-row block stands for complex row 2(t % 4) + t / 8 of the block's 8,
-    // part (t / 4) % 2; with the f64 result layout (row q + 4v in item v) a
-    // lane then holds complex rows 2q (items 0, 1) and 2q + 1 (items 2, 3).
-    const int a_crow = 2 * (c16 & 3) + (c16 >> 3);
-    const int a_ri = (c16 >> 2) & 1;
-    const int a_row = Tr::a_row(c16);
-
-    if (nkt > 0) {
-        load_tiles(0);
-        store_tiles(0, 0);
-        __syncthreads();
-        for (int kt = 0; kt < nkt; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < nkt) load_tiles(kt + 1);
-#pragma unroll
-            for (int s0 = 0; s0 < KS; s0 += CW) {
-                const int kb = q * KS + s0;  // real k of this chunk inside the tile
-                R bf[FN][CW];
+            for (int a = 0; a < FM; ++a) {
+                const int64_t cb = (i0 + wm * WM + a * 16) / 2 + 2 * q;
 #pragma unroll
                 for (int b = 0; b < FN; ++b) {
-                    const u4v v = *reinterpret_cast<const u4v *>(&Bs[buf][wn * WN + b * 16 + c16][kb]);
-                    if constexpr (sizeof(R) == 4) {
-                        const f4 fv = __builtin_bit_cast(f4, v);
+                    const int64_t j = j0 + wn * WN + b * 16 + c16;
+                    if (j >= p.N) continue;
 #pragma unroll
-                        for (int e = 0; e < CW; ++e) bf[b][e] = fv[e];
+                    for (int h = 0; h < 2; ++h) {
+                        const int64_t ic = cb + h;
+                        if (ic >= p.M) continue;
+                        const cplx out = Elem<cplx>::mul(gamma, cplx{acc[a][b][2 * h], acc[a][b][2 * h + 1]});
+                        if (ic < p.split) pD2[ic + j * p.ldd2] = out;
+                        else pD[ic + j * p.ldd] = out;
+                    }
+                }
+            }
+        } else {
+            const R gamma = (R)p.gamma.re;
+#pragma unroll
+            for (int a = 0; a < FM; ++a) {
+                const int64_t r = i0 + wm * WM + a * 16 + 4 * q;
+                if (r >= p.M) continue;
+#pragma unroll
+                for (int b = 0; b < FN; ++b) {
+                    const int64_t j = j0 + wn * WN + b * 16 + c16;
+                    if (j >= p.N) continue;
+                    R out[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) out[v] = gamma * acc[a][b][v];
+                    if (r + 3 < p.split) {
+                        store_rows4<R>(pD2, p.ldd2, p.M, r, j, p.d2_vec, out);
+                    } else if (r >= p.split) {
+                        store_rows4<R>(pD, p.ldd, p.M, r, j, p.d_vec, out);
                     } else {
-                        const d2v dv = __builtin_bit_cast(d2v, v);
-                        bf[b][0] = dv[0];
-                        bf[b][1] = dv[1];
-                    }
-                }
-                R af[FM][CW];
 #pragma unroll
-                for (int a = 0; a < FM; ++a) {
-                    if constexpr (CPLX) {
-                        // real k = kb + e: complex k (kb + e) / 2, part e % 2 (kb even)
-                        const cplx z = As[buf][kb >> 1][(wm * WM + a * 16) / 2 + a_crow];
-                        af[a][0] = a_ri ? z.im : z.re;    // k part 0
-                        af[a][1] = a_ri ? z.re : -z.im;   // k part 1
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < CW; ++e) af[a][e] = As[buf][kb + e][wm * WM + a * 16 + a_row];
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < CW; ++e)
-#pragma unroll
-                    for (int a = 0; a < FM; ++a)
-#pragma unroll
-                        for (int b = 0; b < FN; ++b) acc[a][b] = Tr::mfma(af[a][e], bf[b][e], acc[a][b]);
-            }
-            if (kt + 1 < nkt) {
-                store_tiles(buf ^ 1, kt + 1);
-                __syncthreads();
-            }
-        }
-    }
-
-    // ---- epilogue: D = gamma * acc, rows below `split` to D2 --------------
-    if constexpr (CPLX) {
-        const cplx gamma{p.gamma.re, p.gamma.im};
-#pragma unroll
-        for (int a = 0; a < FM; ++a) {
-            const int64_t cb = (i0 + wm * WM + a * 16) / 2 + 2 * q;
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int64_t j = j0 + wn * WN + b * 16 + c16;
-                if (j >= p.N) continue;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int64_t ic = cb + h;
-                    if (ic >= p.M) continue;
-                    const cplx out = Elem<cplx>::mul(gamma, cplx{acc[a][b][2 * h], acc[a][b][2 * h + 1]});
-                    if (ic < p.split) p.D2[ic + j * p.ldd2] = out;
-                    else p.D[ic + j * p.ldd] = out;
-                }
-            }
-        }
-    } else {
-        const R gamma = (R)p.gamma.re;
-#pragma unroll
-        for (int a = 0; a < FM; ++a) {
-            const int64_t r = i0 + wm * WM + a * 16 + 4 * q;
-            if (r >= p.M) continue;
-#pragma unroll
-            for (int b = 0; b < FN; ++b) {
-                const int64_t j = j0 + wn * WN + b * 16 + c16;
-                if (j >= p.N) continue;
-                R out[4];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) out[v] = gamma * acc[a][b][v];
-                if (r + 3 < p.split) {
-                    store_rows4<R>(p.D2, p.ldd2, p.M, r, j, p.d2_vec, out);
-                } else if (r >= p.split) {
-                    store_rows4<R>(p.D, p.ldd, p.M, r, j, p.d_vec, out);
-                } else {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int64_t ii = r + v;
-                        if (ii >= p.M) break;
-                        if (ii < p.split) p.D2[ii + j * p.ldd2] = out[v];
-                        else p.D[ii + j * p.ldd] = out[v];
+                        for (int v = 0; v < 4; ++v) {
+                            const int64_t ii = r + v;
+                            if (ii >= p.M) break;
+                            if (ii < p.split) pD2[ii + j * p.ldd2] = out[v];
+                            else pD[ii + j * p.ldd] = out[v];
+                        }
                     }
                 }
             }
         }
-    }
+    }  // pass
 }
 
 inline bool aligned16(const void *ptr, int64_t ld, size_t es) {
@@ -530,7 +543,8 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
         if (!al(g.sCo, g.sCi)) p.c_vec = 0;
         if (!al(g.sDo, g.sDi)) p.d_vec = p.d2_vec = 0;
     }
-    const dim3 grid((unsigned)(tM * tN), (unsigned)nz);
+    const int64_t rowsM = g.a_lower ? (tM + 1) / 2 : tM;  // triangular: pairs of row tiles
+    const dim3 grid((unsigned)(rowsM * tN), (unsigned)nz);
     const bool vec = p.a_vec && p.b_vec;
     if (g.a_lower) {
         if (vec) hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, true, true>), grid, dim3(256), 0, st, p);
@@ -544,14 +558,17 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
 
 // Macro tile, from timings on MI355X of the update and solve sequences of
 // blocked solves (fp32 4096^2, fp64 1024^2 .. 8192^2, complex 8192 x 2048):
-// 64 x 64 for the triangular products, for fp32 and for small launches; for
-// large updates 128 x 64 (fp64) or 64 x 128 (complex, whose 64 real rows are
-// 32 complex rows) once that shape gives at least 1024 tiles, four per CU.
-// A 128 x 128 tile needs ~250 VGPRs and 70 KB of LDS, which leaves too few
-// waves per CU to cover its loads; it lost on every shape measured.
+// 64 x 32 for the triangular products (each workgroup folds two row tiles,
+// so twice as many column tiles keep the CUs busy); 64 x 64 for fp32 and for
+// small or batched launches; for large updates 128 x 64 (fp64) or 64 x 128
+// (complex, whose 64 real rows are 32 complex rows) once that shape gives at
+// least 1024 tiles, four per CU.  A 128 x 128 tile needs ~250 VGPRs and 70 KB
+// of LDS, which leaves too few waves per CU to cover its loads; it lost on
+// every shape measured.
 template <typename T, int KT>
 hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
-    if (!g.a_lower && g.batch <= 1) {
+    if (g.a_lower) return launch_tile<T, 64, 32, KT>(g, st);
+    if (g.batch <= 1) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
         if constexpr (GemmTraits<T>::kCplx) {
             if (((Mr + 63) / 64) * ((g.N + 127) / 128) >= 1024) return launch_tile<T, 64, 128, KT>(g, st);
