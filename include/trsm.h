@@ -97,7 +97,7 @@ trsm_status_t trsm_lln_strided_batched(trsm_dtype_t dtype, int64_t m, int64_t n,
 /*
  * trsm_lln with a forced diagonal block size (section 4.3.2 of the pages:
  * the offline sweep times each candidate).  ib == 0 uses the table; any
- * other value must be 64, 128, 256 or 512, else INVALID_VALUE.  For m <= 64
+ * other value must be 64, 128, 256, 512 or 1024, else INVALID_VALUE.  For m <= 64
  * ib is ignored (direct solve), unless force_blocked != 0, which runs the
  * blocked path at any m > 0.
  */

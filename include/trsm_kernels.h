@@ -30,7 +30,7 @@ extern "C" {
  * cores; for ib > 64 the scratch of that step comes from the library's
  * per-(device, stream) workspace (TRSM_STATUS_ALLOC_FAILED if it cannot
  * grow).
- * ib in {64, 128, 256, 512}; m >= 0.
+ * ib in {64, 128, 256, 512, 1024}; m >= 0.
  */
 trsm_status_t trsm_kernel_diag_inv(trsm_dtype_t dtype, int ib, int64_t m, const void *A,
                                    int64_t lda, void *W, hipStream_t stream);

@@ -122,10 +122,10 @@ def test_regime_edges(T, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
-@pytest.mark.parametrize("ib", [64, 128, 256, 512])
+@pytest.mark.parametrize("ib", [64, 128, 256, 512, 1024])
 def test_every_block_size_ragged(T, dtype, ib):
-    """m = 1000 is a multiple of no candidate block size; n = 257 is ragged
-    against the GEMM tiles."""
+    """m = 1000 is a multiple of no candidate block size (below 1024 it is
+    one ragged block); n = 257 is ragged against the GEMM tiles."""
     m, n = 1000, 257
     L, B = make_problem(dtype, m, n, seed=ib)
     a = 0.75 + 0.5j if dtype == "c64" else 0.75

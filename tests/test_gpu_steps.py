@@ -124,7 +124,7 @@ def test_gemm_k_zero_and_gamma_zero(T, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
-@pytest.mark.parametrize("ib", [64, 128, 256, 512])
+@pytest.mark.parametrize("ib", [64, 128, 256, 512, 1024])
 def test_diag_inv_vs_oracle_identity_solve(T, dtype, ib):
     import torch
     m = ib * 2 + 37  # two full blocks and a ragged one

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libtrsm_amd.so")
 
 R32F, R64F, C64F = 0, 1, 2
 STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "ALLOC_FAILED", 3: "HIP_ERROR", 4: "NOT_SUPPORTED"}
-IB_CHOICES = (64, 128, 256, 512)
+IB_CHOICES = (64, 128, 256, 512, 1024)
 
 # Every symbol include/trsm.h and include/trsm_kernels.h declare.
 EXPORTS = ("trsm_lln", "trsm_lln_strided_batched", "trsm_lln_ex", "trsm_lln_select_ib",

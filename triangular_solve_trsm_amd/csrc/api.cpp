@@ -179,6 +179,8 @@ trsm_status_t check_args(int dt, int64_t m, int64_t n, const void *alpha, const 
 
 trsm_status_t hip_status(hipError_t e) { return e == hipSuccess ? TRSM_STATUS_SUCCESS : TRSM_STATUS_HIP_ERROR; }
 
+bool valid_ib(int ib) { return ib == 64 || ib == 128 || ib == 256 || ib == 512 || ib == 1024; }
+
 int select_ib(int dt, int64_t m) {
     int best = 256;
     int64_t bestd = INT64_MAX;
@@ -354,7 +356,7 @@ trsm_status_t trsm_lln_ex(trsm_dtype_t dtype, int64_t m, int64_t n, const void *
                           const void *A, int64_t lda, void *B, int64_t ldb, int ib,
                           int force_blocked, hipStream_t stream) {
     try {
-        if (ib != 0 && ib != 64 && ib != 128 && ib != 256 && ib != 512)
+        if (ib != 0 && !valid_ib(ib))
             return TRSM_STATUS_INVALID_VALUE;
         trsm_status_t s = check_args(dtype, m, n, alpha, A, lda, B, ldb);
         if (s != TRSM_STATUS_SUCCESS) return s;
@@ -368,7 +370,7 @@ trsm_status_t trsm_kernel_diag_inv(trsm_dtype_t dtype, int ib, int64_t m, const 
                                    int64_t lda, void *W, hipStream_t stream) {
     try {
         if (!valid_dtype(dtype) || m < 0 || lda < (m > 1 ? m : 1)) return TRSM_STATUS_INVALID_VALUE;
-        if (ib != 64 && ib != 128 && ib != 256 && ib != 512) return TRSM_STATUS_INVALID_VALUE;
+        if (!valid_ib(ib)) return TRSM_STATUS_INVALID_VALUE;
         if (m == 0) return TRSM_STATUS_SUCCESS;
         if (A == nullptr || W == nullptr) return TRSM_STATUS_INVALID_VALUE;
         int dev = 0;

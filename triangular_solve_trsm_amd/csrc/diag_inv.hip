@@ -229,7 +229,7 @@ int64_t diag_inv_tmp_elems(int ib, int64_t m) {
 
 hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t lda, void *W,
                            void *tmp, hipStream_t stream) {
-    if (ib != 64 && ib != 128 && ib != 256 && ib != 512) return hipErrorInvalidValue;
+    if (ib != 64 && ib != 128 && ib != 256 && ib != 512 && ib != 1024) return hipErrorInvalidValue;
     if (m <= 0) return hipSuccess;
     hipError_t e = launch_base(dtype, m, A, lda, W, ib, stream);
     if (e != hipSuccess || ib <= kBase) return e;

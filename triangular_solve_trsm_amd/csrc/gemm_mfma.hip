@@ -535,7 +535,7 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
     p.sAo = g.sAo; p.sAi = g.sAi; p.sBo = g.sBo; p.sBi = g.sBi;
     p.sCo = g.sCo; p.sCi = g.sCi; p.sDo = g.sDo; p.sDi = g.sDi;
     if (nz > 1) {
-        if (g.split != 0 || g.binner < 1 || g.binner > nz) return hipErrorInvalidValue;
+        if (g.split != 0 || g.binner < 1) return hipErrorInvalidValue;
         // every problem's operands keep the alignment of the first
         const auto al = [&](int64_t o, int64_t i) { return (o * (int64_t)es) % 16 == 0 && (i * (int64_t)es) % 16 == 0; };
         if (!al(g.sAo, g.sAi)) p.a_vec = 0;
@@ -559,10 +559,10 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
 // Macro tile, from timings on MI355X of the update and solve sequences of
 // blocked solves (fp32 4096^2, fp64 1024^2 .. 8192^2, complex 8192 x 2048):
 // 64 x 32 for the triangular products (each workgroup folds two row tiles,
-// so twice as many column tiles keep the CUs busy); 64 x 64 for fp32 and for
-// small or batched launches; for large updates 128 x 64 (fp64) or 64 x 128
-// (complex, whose 64 real rows are 32 complex rows) once that shape gives at
-// least 1024 tiles, four per CU.  A 128 x 128 tile needs ~250 VGPRs and 70 KB
+// so twice as many column tiles keep the CUs busy) and for updates too small
+// to give 1024 tiles of 64 x 64; 64 x 64 for fp32 and batched launches; for
+// large updates 128 x 64 (fp64) or 64 x 128 (complex, whose 64 real rows are
+// 32 complex rows) once that shape gives at least 1024 tiles, four per CU.  A 128 x 128 tile needs ~250 VGPRs and 70 KB
 // of LDS, which leaves too few waves per CU to cover its loads; it lost on
 // every shape measured.
 template <typename T, int KT>
@@ -575,6 +575,7 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
         } else if constexpr (sizeof(T) == 8) {
             if (((Mr + 127) / 128) * ((g.N + 63) / 64) >= 1024) return launch_tile<T, 128, 64, KT>(g, st);
         }
+        if (((Mr + 63) / 64) * ((g.N + 63) / 64) < 1024) return launch_tile<T, 64, 32, KT>(g, st);
     }
     return launch_tile<T, 64, 64, KT>(g, st);
 }

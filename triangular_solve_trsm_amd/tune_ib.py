@@ -29,7 +29,7 @@ ROOT = os.path.dirname(HERE)
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-CANDIDATES = (64, 128, 256, 512)
+CANDIDATES = (64, 128, 256, 512, 1024)
 DTYPES = (("f32", "R32F"), ("f64", "R64F"), ("c64", "C64F"))
 DEFAULT_SIZES = (128, 256, 512, 1024, 2048, 4096, 8192, 16384)
 
