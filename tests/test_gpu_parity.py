@@ -134,6 +134,22 @@ def test_every_block_size_ragged(T, dtype, ib):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("schedule", ["left", "right"])
+@pytest.mark.parametrize("ib", [128, 256])
+def test_both_phase2_schedules(T, dtype, schedule, ib, monkeypatch):
+    """Left-looking (each block row updated once with K = r*ib) and
+    right-looking phase 2 forced in turn: m = 1000 leaves a ragged last block
+    row, n = 257 a ragged column tile, alpha != 1 checks that the scaling is
+    applied exactly once per element."""
+    monkeypatch.setenv("TRSM_SCHEDULE", schedule)
+    m, n = 1000, 257
+    L, B = make_problem(dtype, m, n, seed=7 + ib)
+    a = -1.25 + 0.5j if dtype == "c64" else -1.25
+    X = solve_gpu(T, L, B, a, ib=ib)
+    check(dtype, X, oracle.solve(L, B, a), f"{dtype} {schedule} ib={ib}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
 def test_m_4097_narrow(T, dtype):
     m, n = 4097, 19
     L, B = make_problem(dtype, m, n, seed=4097)

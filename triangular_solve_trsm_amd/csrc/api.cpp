@@ -41,6 +41,7 @@ struct IbEntry {
     int dtype;
     int64_t m;
     int ib;
+    int left;  // phase-2 schedule that measured faster: 1 left-looking, 0 right-looking
 };
 #include "ib_table.inc"
 
@@ -179,25 +180,50 @@ trsm_status_t check_args(int dt, int64_t m, int64_t n, const void *alpha, const 
 
 trsm_status_t hip_status(hipError_t e) { return e == hipSuccess ? TRSM_STATUS_SUCCESS : TRSM_STATUS_HIP_ERROR; }
 
+// Left-looking once an update has this many 64 x 64 tiles (four per CU).
+constexpr int64_t kLeftMinTiles = 1024;
+
 bool valid_ib(int ib) { return ib == 64 || ib == 128 || ib == 256 || ib == 512 || ib == 1024; }
 
-int select_ib(int dt, int64_t m) {
-    int best = 256;
+// Nearest tabulated order for this data type (section 4.3.2: online lookup).
+IbEntry select_entry(int dt, int64_t m) {
+    IbEntry best{dt, 0, 256, 0};
     int64_t bestd = INT64_MAX;
     for (const IbEntry &e : kIbTable) {
         if (e.dtype != dt) continue;
         const int64_t d = e.m > m ? e.m - m : m - e.m;
         if (d < bestd) {
             bestd = d;
-            best = e.ib;
+            best = e;
         }
     }
     return best;
 }
 
+int select_ib(int dt, int64_t m) { return select_entry(dt, m).ib; }
+
+// Phase 2 schedule.  Left-looking is the pages' order (section 4.3 "Phase 2"):
+// block row r+1 is updated once, by all solved rows, with K = (r+1)*ib.
+// Right-looking (each solved block row updates every row below it, M = rows
+// left) does the same arithmetic in another order.  The offline sweep
+// records which one measured faster for each (data type, order); a left-
+// looking update has only ib rows, so a narrow B, which gives it too few
+// tiles, stays right-looking.  TRSM_SCHEDULE=left|right overrides both
+// (tuning and tests).
+bool use_left_looking(int dt, int64_t m, int64_t n, int ib, bool table_left) {
+    const char *e = std::getenv("TRSM_SCHEDULE");
+    if (e && std::strcmp(e, "left") == 0) return true;
+    if (e && std::strcmp(e, "right") == 0) return false;
+    if (!table_left) return false;
+    const int64_t rows = (dt == C64F ? 2 : 1) * (int64_t)(ib < m ? ib : m);  // real rows of an update
+    return ((rows + 63) / 64) * ((n + 63) / 64) >= kLeftMinTiles;
+}
+
 // Blocked path for one problem (m > 0, n > 0, alpha != 0).
 trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void *A,
-                          int64_t lda, void *B, int64_t ldb, int ib, int dev, hipStream_t st) {
+                          int64_t lda, void *B, int64_t ldb, int ib, bool table_left, int dev,
+                          hipStream_t st) {
+    const bool left = use_left_looking(dt, m, n, ib, table_left);
     const size_t es = dtype_size(dt);
     const int64_t nb = (m + ib - 1) / ib;
     size_t wbytes = (size_t)nb * ib * ib * es;
@@ -215,8 +241,8 @@ trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void
     const char *Ab = static_cast<const char *>(A);
     char *Bb = static_cast<char *>(B);
     if (log_enabled())
-        std::fprintf(stderr, "[trsm] blocked dtype=%d m=%lld n=%lld ib=%d nb=%lld\n", dt,
-                     (long long)m, (long long)n, ib, (long long)nb);
+        std::fprintf(stderr, "[trsm] blocked dtype=%d m=%lld n=%lld ib=%d nb=%lld %s-looking\n", dt,
+                     (long long)m, (long long)n, ib, (long long)nb, left ? "left" : "right");
 
     hipError_t e;
     {
@@ -260,9 +286,33 @@ trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void
         }
         if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
         if (r + 1 == nb) break;
-        // update: rows below block r
         const int64_t mrest = m - r0 - bs;
         const int64_t bsn = mrest < ib ? mrest : ib;
+        if (left) {
+            // next block row: P = alpha B_{r+1} - L[r+1, 0:r+1] X[0:r+1]
+            GemmDesc ug{};
+            ug.M = bsn;
+            ug.N = n;
+            ug.K = r0 + bs;
+            ug.A = Ab + (size_t)(r0 + bs) * es;
+            ug.lda = lda;
+            ug.Bm = Bb;
+            ug.ldb = ldb;
+            ug.C = Bb + (size_t)(r0 + bs) * es;
+            ug.ldc = ldb;
+            ug.D = P;
+            ug.ldd = ib;
+            ug.ldd2 = ib;
+            ug.beta = alpha;
+            ug.gamma = minus_one;
+            {
+                LaunchTimer t(TRSM_KERNEL_UPDATE_GEMM, dt, bsn, n, r0 + bs, 1, st);
+                e = gemm_launch(dt, ug, st);
+            }
+            if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+            continue;
+        }
+        // update: rows below block r
         GemmDesc ug{};
         ug.M = mrest;
         ug.N = n;
@@ -310,11 +360,13 @@ trsm_status_t run(int dt, int64_t m, int64_t n, const void *alpha_p, const void 
         LaunchTimer t(TRSM_KERNEL_SMALL, dt, m, n, 0, batch, st);
         return hip_status(small_lln_launch(dt, (int)m, n, alpha, A, lda, sA, B, ldb, sB, batch, st));
     }
-    const int ib = ib_forced ? ib_forced : select_ib(dt, m);
+    const IbEntry cfg = select_entry(dt, m);
+    const int ib = ib_forced ? ib_forced : cfg.ib;
     const size_t es = dtype_size(dt);
     for (int64_t p = 0; p < batch; ++p) {
         s = run_blocked(dt, m, n, alpha, static_cast<const char *>(A) + (size_t)(p * sA) * es, lda,
-                        static_cast<char *>(B) + (size_t)(p * sB) * es, ldb, ib, dev, st);
+                        static_cast<char *>(B) + (size_t)(p * sB) * es, ldb, ib, cfg.left != 0,
+                        dev, st);
         if (s != TRSM_STATUS_SUCCESS) return s;
     }
     return TRSM_STATUS_SUCCESS;

@@ -26,9 +26,10 @@
 //     main loop;
 //   * operands are staged through LDS, double-buffered: the loads of K tile
 //     t+1 are in flight while the MFMAs of tile t run, one barrier per tile.
-//     A is kept as [k][row] (its global layout), Bm as [column][k] (its
-//     global layout too), with pads that spread the fragment reads over all
-//     LDS banks;
+//     A is kept as [k][row] (its global layout) with an XOR swizzle of the
+//     row index, Bm as [column][k] (its global layout too) with a padded
+//     pitch, so that the fragment reads of the four lane groups spread over
+//     all LDS banks;
 //   * inside a K tile lane group q (lane / 16) works on k = q*KT/4 ... so
 //     each lane's Bm fragments for consecutive MFMAs are adjacent in LDS and
 //     come in 16-byte reads (the order of a sum over k is free);
@@ -198,10 +199,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     constexpr int AK = CPLX ? KT / 2 : KT;
     constexpr int AR = CPLX ? MT / 2 : MT;
     constexpr int AU = CPLX ? 1 : VR;  // elements of T per 16-byte load
-    constexpr int SA = AR + 4;         // row pitch: lane groups land 32 banks apart
+    constexpr int SA = AR + 4;         // row pitch (16-byte multiple)
+    // Swizzle of the A tile.  Lane group q reads k rows [q*KPG, q*KPG + KPG)
+    // of the tile, and with any 16-byte pitch those start 0 or 32 banks
+    // apart, so groups 0 and 2 (1 and 3) hit the same banks.  Row r of k
+    // row kk is stored at r ^ swz(kk): 16 dwords further in every other
+    // pair of groups, which puts the four groups on four distinct sets of
+    // 16 banks; the XOR keeps each 16-byte store contiguous.
+    constexpr int KPG = CPLX ? KS / 2 : KS;  // A-tile k rows per lane group
+    constexpr int SW = 64 / (int)sizeof(T);  // elements in 16 dwords
+    static_assert(AR >= 2 * SW && SW % AU == 0, "A swizzle");
     constexpr int SB = KT + (VR == 4 ? 4 : 2);  // 36 (f32) / 18 (f64) reals: 9 x 16 bytes
     __shared__ __attribute__((aligned(16))) T As[2][AK][SA];
     __shared__ __attribute__((aligned(16))) R Bs[2][NT][SB];
+    const auto a_swz = [](int kk) { return ((kk / KPG) & 1) * SW; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -294,14 +305,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         static_assert(B_PASSES * B_CPP == NT, "B tile shape");
         constexpr int DW = (int)sizeof(R) / 4;  // dwords per real
 
-        u4v ra[A_PASSES];
-        u4v rb[B_PASSES];
+        // Register staging sets: with DEPTH 2 the loads of tile kt+2 are in
+        // flight while tile kt+1 waits in the other set, so a load has two
+        // tiles of products to arrive.  Small tiles run few products per K
+        // tile and need that; the 128-row tiles keep one set (their register
+        // budget decides how many waves a SIMD holds).
+        constexpr int DEPTH = (MT * NT <= 64 * 64) ? 2 : 1;
+        u4v ra[DEPTH][A_PASSES];
+        u4v rb[DEPTH][B_PASSES];
 
         // Loads of K tile kt into registers.  The ragged-K mask is applied when
         // the registers are written to LDS (store_tiles), not here: a select on
         // the loaded values would make the compiler wait for the loads right
         // after issuing them, before the MFMAs they are meant to overlap.
-        auto load_tiles = [&](int kt) {
+        auto load_tiles = [&](int kt, auto set_c) {
+            constexpr int S = decltype(set_c)::value;
             const int64_t k0 = (int64_t)kt * KT;  // real k offset
             const int64_t k0t = CPLX ? k0 / 2 : k0;
             {
@@ -313,7 +331,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
                     const int kk = flat / A_TPC;
                     const int rr = flat - kk * A_TPC;
                     const uint32_t boff = (uint32_t)(((int64_t)rr * AU + (int64_t)kk * p.lda) * (int64_t)sizeof(T));
-                    ra[s] = ld16<VEC>(rs, boff);
+                    ra[S][s] = ld16<VEC>(rs, boff);
                 }
             }
             {
@@ -326,14 +344,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
                     const int kv = (flat - jj * B_TPC) * VR;  // real k inside the tile
                     const int64_t kvt = CPLX ? kv / 2 : kv;
                     const uint32_t boff = (uint32_t)((kvt + (int64_t)jj * p.ldb) * (int64_t)sizeof(T));
-                    rb[s] = ld16<VEC>(rs, boff);
+                    rb[S][s] = ld16<VEC>(rs, boff);
                 }
             }
         };
 
         // Registers of K tile kt -> LDS buffer buf; entries with k >= K become
         // zero (only the last, ragged K tile has any: a uniform test first).
-        auto store_tiles = [&](int buf, int kt) {
+        auto store_tiles = [&](int buf, int kt, auto set_c) {
+            constexpr int S = decltype(set_c)::value;
             const int64_t k0 = (int64_t)kt * KT;
             const int64_t k0t = CPLX ? k0 / 2 : k0;
             const bool ragged = k0 + KT > Kr;  // wave-uniform
@@ -342,16 +361,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
                 const int flat = s * 256 + tid;
                 const int kk = flat / A_TPC;
                 const int rr = flat - kk * A_TPC;
-                u4v v = ra[s];
+                u4v v = ra[S][s];
                 if (ragged && k0t + kk >= p.K) v = u4v{0u, 0u, 0u, 0u};
-                *reinterpret_cast<u4v *>(&As[buf][kk][rr * AU]) = v;
+                *reinterpret_cast<u4v *>(&As[buf][kk][(rr * AU) ^ a_swz(kk)]) = v;
             }
 #pragma unroll
             for (int s = 0; s < B_PASSES; ++s) {
                 const int flat = s * 256 + tid;
                 const int jj = flat / B_TPC;
                 const int kv = (flat - jj * B_TPC) * VR;
-                u4v v = rb[s];
+                u4v v = rb[S][s];
                 if (ragged) {
 #pragma unroll
                     for (int e = 0; e < VR; ++e)
@@ -371,53 +390,83 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         const int a_ri = (c16 >> 2) & 1;
         const int a_row = Tr::a_row(c16);
 
-        if (nkt > 0) {
-            load_tiles(0);
-            store_tiles(0, 0);
-            __syncthreads();
-            for (int kt = 0; kt < nkt; ++kt) {
-                const int buf = kt & 1;
-                if (kt + 1 < nkt) load_tiles(kt + 1);
+        // Products of the K tile in LDS buffer buf.
+        auto mfma_tile = [&](const int buf) {
 #pragma unroll
-                for (int s0 = 0; s0 < KS; s0 += CW) {
-                    const int kb = q * KS + s0;  // real k of this chunk inside the tile
-                    R bf[FN][CW];
+            for (int s0 = 0; s0 < KS; s0 += CW) {
+                const int kb = q * KS + s0;  // real k of this chunk inside the tile
+                R bf[FN][CW];
 #pragma unroll
-                    for (int b = 0; b < FN; ++b) {
-                        const u4v v = *reinterpret_cast<const u4v *>(&Bs[buf][wn * WN + b * 16 + c16][kb]);
-                        if constexpr (sizeof(R) == 4) {
-                            const f4 fv = __builtin_bit_cast(f4, v);
+                for (int b = 0; b < FN; ++b) {
+                    const u4v v = *reinterpret_cast<const u4v *>(&Bs[buf][wn * WN + b * 16 + c16][kb]);
+                    if constexpr (sizeof(R) == 4) {
+                        const f4 fv = __builtin_bit_cast(f4, v);
 #pragma unroll
-                            for (int e = 0; e < CW; ++e) bf[b][e] = fv[e];
-                        } else {
-                            const d2v dv = __builtin_bit_cast(d2v, v);
-                            bf[b][0] = dv[0];
-                            bf[b][1] = dv[1];
-                        }
+                        for (int e = 0; e < CW; ++e) bf[b][e] = fv[e];
+                    } else {
+                        const d2v dv = __builtin_bit_cast(d2v, v);
+                        bf[b][0] = dv[0];
+                        bf[b][1] = dv[1];
                     }
-                    R af[FM][CW];
-#pragma unroll
-                    for (int a = 0; a < FM; ++a) {
-                        if constexpr (CPLX) {
-                            // real k = kb + e: complex k (kb + e) / 2, part e % 2 (kb even)
-                            const cplx z = As[buf][kb >> 1][(wm * WM + a * 16) / 2 + a_crow];
-                            af[a][0] = a_ri ? z.im : z.re;    // k part 0
-                            af[a][1] = a_ri ? z.re : -z.im;   // k part 1
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < CW; ++e) af[a][e] = As[buf][kb + e][wm * WM + a * 16 + a_row];
-                        }
-                    }
-#pragma unroll
-                    for (int e = 0; e < CW; ++e)
-#pragma unroll
-                        for (int a = 0; a < FM; ++a)
-#pragma unroll
-                            for (int b = 0; b < FN; ++b) acc[a][b] = Tr::mfma(af[a][e], bf[b][e], acc[a][b]);
                 }
-                if (kt + 1 < nkt) {
-                    store_tiles(buf ^ 1, kt + 1);
-                    __syncthreads();
+                R af[FM][CW];
+#pragma unroll
+                for (int a = 0; a < FM; ++a) {
+                    if constexpr (CPLX) {
+                        // real k = kb + e: complex k (kb + e) / 2, part e % 2 (kb even)
+                        const cplx z = As[buf][kb >> 1][((wm * WM + a * 16) / 2 + a_crow) ^ a_swz(kb >> 1)];
+                        af[a][0] = a_ri ? z.im : z.re;    // k part 0
+                        af[a][1] = a_ri ? z.re : -z.im;   // k part 1
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < CW; ++e)
+                            af[a][e] = As[buf][kb + e][(wm * WM + a * 16 + a_row) ^ a_swz(kb + e)];
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < CW; ++e)
+#pragma unroll
+                    for (int a = 0; a < FM; ++a)
+#pragma unroll
+                        for (int b = 0; b < FN; ++b) acc[a][b] = Tr::mfma(af[a][e], bf[b][e], acc[a][b]);
+            }
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        if (nkt > 0) {
+            if constexpr (DEPTH == 2) {
+                load_tiles(0, I0{});
+                if (nkt > 1) load_tiles(1, I1{});
+                store_tiles(0, 0, I0{});
+                __syncthreads();
+                // step kt (kt % 2 == S): set S held tile kt (already in LDS)
+                // and takes tile kt+2; tile kt+1 goes from set S^1 to buffer S^1
+                auto step = [&](int kt, auto set_c) {
+                    constexpr int S = decltype(set_c)::value;
+                    using IN = std::integral_constant<int, S ^ 1>;
+                    if (kt + 2 < nkt) load_tiles(kt + 2, set_c);
+                    mfma_tile(S);
+                    if (kt + 1 < nkt) {
+                        store_tiles(S ^ 1, kt + 1, IN{});
+                        __syncthreads();
+                    }
+                };
+                for (int kt = 0; kt < nkt; kt += 2) {
+                    step(kt, I0{});
+                    if (kt + 1 < nkt) step(kt + 1, I1{});
+                }
+            } else {
+                load_tiles(0, I0{});
+                store_tiles(0, 0, I0{});
+                __syncthreads();
+                for (int kt = 0; kt < nkt; ++kt) {
+                    const int buf = kt & 1;
+                    if (kt + 1 < nkt) load_tiles(kt + 1, I0{});
+                    mfma_tile(buf);
+                    if (kt + 1 < nkt) {
+                        store_tiles(buf ^ 1, kt + 1, I0{});
+                        __syncthreads();
+                    }
                 }
             }
         }
@@ -558,26 +607,31 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
 
 // Macro tile, from timings on MI355X of the update and solve sequences of
 // blocked solves (fp32 4096^2, fp64 1024^2 .. 8192^2, complex 8192 x 2048):
-// 64 x 32 for the triangular products (each workgroup folds two row tiles,
-// so twice as many column tiles keep the CUs busy) and for updates too small
-// to give 1024 tiles of 64 x 64; 64 x 64 for fp32 and batched launches; for
-// large updates 128 x 64 (fp64) or 64 x 128 (complex, whose 64 real rows are
-// 32 complex rows) once that shape gives at least 1024 tiles, four per CU.  A 128 x 128 tile needs ~250 VGPRs and 70 KB
-// of LDS, which leaves too few waves per CU to cover its loads; it lost on
-// every shape measured.
+//   * 64 x 32 for the triangular products (each workgroup folds two row
+//     tiles, so twice as many column tiles keep the CUs busy), for updates
+//     too small to give 1024 tiles of 64 x 64, and for batched launches (the
+//     small products of the diagonal inversion);
+//   * 128 x 64 (fp64) or 64 x 128 (complex, whose 64 real rows are 32
+//     complex rows) for updates that give at least 2048 such tiles: at three
+//     of these workgroups per CU, fewer leave a last round that runs the
+//     chip part empty;
+//   * 64 x 64 otherwise.
+// A 128 x 128 tile needs ~250 VGPRs and 70 KB of LDS, which leaves too few
+// waves per CU to cover its loads; it lost on every shape measured.
 template <typename T, int KT>
 hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
     if (g.a_lower) return launch_tile<T, 64, 32, KT>(g, st);
     if (g.batch <= 1) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
         if constexpr (GemmTraits<T>::kCplx) {
-            if (((Mr + 63) / 64) * ((g.N + 127) / 128) >= 1024) return launch_tile<T, 64, 128, KT>(g, st);
+            if (((Mr + 63) / 64) * ((g.N + 127) / 128) >= 2048) return launch_tile<T, 64, 128, KT>(g, st);
         } else if constexpr (sizeof(T) == 8) {
-            if (((Mr + 127) / 128) * ((g.N + 63) / 64) >= 1024) return launch_tile<T, 128, 64, KT>(g, st);
+            if (((Mr + 127) / 128) * ((g.N + 63) / 64) >= 2048) return launch_tile<T, 128, 64, KT>(g, st);
         }
         if (((Mr + 63) / 64) * ((g.N + 63) / 64) < 1024) return launch_tile<T, 64, 32, KT>(g, st);
+        return launch_tile<T, 64, 64, KT>(g, st);
     }
-    return launch_tile<T, 64, 64, KT>(g, st);
+    return launch_tile<T, 64, 32, KT>(g, st);  // batched: the small products of the inversion
 }
 
 }  // namespace

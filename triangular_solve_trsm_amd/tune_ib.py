@@ -6,6 +6,9 @@ phases: offline, every candidate block size is timed for each (matrix scale,
 data type) and only the fastest is kept in a table; online, the library looks
 up the entry of the nearest tabulated scale.  This script is the offline
 phase for MI355X; the online lookup is trsm_lln_select_ib in the library.
+Besides the block size, each point times both orders of phase 2 (left-looking
+as in section 4.3 "Phase 2", and right-looking) and the table keeps the
+faster pair.
 
 Protocol (section 5.1 of the pages): square problems (m = n), inputs drawn by
 trsm_inputs, each point run 10 times, the first discarded, the mean of the
@@ -34,10 +37,11 @@ DTYPES = (("f32", "R32F"), ("f64", "R64F"), ("c64", "C64F"))
 DEFAULT_SIZES = (128, 256, 512, 1024, 2048, 4096, 8192, 16384)
 
 
-def time_point(T, torch, L, B, alpha, ib, runs=10):
-    import numpy as np
-    Ad = torch.from_numpy(np.ascontiguousarray(L.T)).cuda().T
-    B0 = torch.from_numpy(np.ascontiguousarray(B.T)).cuda().T
+SCHEDULES = ("right", "left")
+
+
+def time_point(T, torch, Ad, B0, alpha, ib, schedule, runs=10):
+    os.environ["TRSM_SCHEDULE"] = schedule
     Bd = B0.clone()
     times = []
     for _ in range(runs):
@@ -50,6 +54,7 @@ def time_point(T, torch, L, B, alpha, ib, runs=10):
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
+    del Bd
     return sum(times[1:]) / (runs - 1)
 
 
@@ -70,22 +75,27 @@ def main():
     device = f"{getattr(props, 'gcnArchName', props.name)} ({props.multi_processor_count} CUs)"
     results = []
     best = {}
+    import numpy as np
     for dt, code in DTYPES:
         for m in sizes:
             L, B = make_problem(dt, m, m, seed=20261300 + m)
+            Ad = torch.from_numpy(np.ascontiguousarray(L.T)).cuda().T
+            B0 = torch.from_numpy(np.ascontiguousarray(B.T)).cuda().T
+            del L, B
             alpha = 1.0 + 0j if dt == "c64" else 1.0
             row = {}
             for ib in CANDIDATES:
                 if ib > m:
                     continue
-                ms = time_point(T, torch, L, B, alpha, ib)
-                row[ib] = ms
-                results.append({"dtype": dt, "m": m, "ib": ib, "ms": ms})
-                print(json.dumps(results[-1]), flush=True)
-            ib_best = min(row, key=row.get)
-            best[(code, m)] = (ib_best, row)
-            del L, B
+                for sch in SCHEDULES:
+                    ms = time_point(T, torch, Ad, B0, alpha, ib, sch)
+                    row[(ib, sch)] = ms
+                    results.append({"dtype": dt, "m": m, "ib": ib, "schedule": sch, "ms": ms})
+                    print(json.dumps(results[-1]), flush=True)
+            best[(code, m)] = (min(row, key=row.get), row)
+            del Ad, B0
             torch.cuda.empty_cache()
+    os.environ.pop("TRSM_SCHEDULE", None)
 
     stamp = datetime.date.today().isoformat()
     lines = [
@@ -93,12 +103,15 @@ def main():
         "// nearest-order match (section 4.3.2 of the pages: offline profiling,",
         "// online lookup).  Written by triangular_solve_trsm_amd/tune_ib.py on",
         f"// {device}, {stamp}: square problems, mean of runs 2-10 per point.",
-        "// Each entry's comment lists the time in ms of every candidate.",
+        "// Fields: data type, order, block size, phase-2 order (1 left-looking,",
+        "// 0 right-looking).  Each entry's comment lists the time in ms of every",
+        "// candidate block size, right-looking / left-looking.",
         "static const IbEntry kIbTable[] = {",
     ]
-    for (code, m), (ib, row) in best.items():
-        times = ", ".join(f"{c}: {row[c]:.3f}" for c in sorted(row))
-        lines.append(f"    {{{code}, {m}, {ib}}},  // {times}")
+    for (code, m), ((ib, sch), row) in best.items():
+        ibs = sorted({c for c, _ in row})
+        times = ", ".join(f"{c}: {row[(c, 'right')]:.3f}/{row[(c, 'left')]:.3f}" for c in ibs)
+        lines.append(f"    {{{code}, {m}, {ib}, {1 if sch == 'left' else 0}}},  // {times}")
     lines.append("};")
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
