@@ -10,8 +10,9 @@
  *     L X = alpha B,   x_ij = (alpha b_ij - sum_{k<i} l_ik x_kj) / l_ii.
  *
  * Data layout: column-major; element (i, j) of A is A[i + j*lda] and of B is
- * B[i + j*ldb].  Complex data (TRSM_C64F) are interleaved (re, im) pairs of
- * doubles, layout-compatible with hipDoubleComplex; no operand is conjugated.
+ * B[i + j*ldb].  Complex data are interleaved (re, im) pairs: of doubles for
+ * TRSM_C64F (layout-compatible with hipDoubleComplex), of floats for
+ * TRSM_C32F (hipFloatComplex); no operand is conjugated.
  *
  * Ownership: A and B are device pointers owned by the caller, who keeps them
  * alive until the work enqueued on `stream` has completed.  alpha is a host
@@ -57,14 +58,16 @@ typedef enum trsm_status_t {
 typedef enum trsm_dtype_t {
     TRSM_R32F = 0, /* float                                   */
     TRSM_R64F = 1, /* double                                  */
-    TRSM_C64F = 2  /* complex double, interleaved (re, im)    */
+    TRSM_C64F = 2, /* complex double, interleaved (re, im)    */
+    TRSM_C32F = 3  /* complex float, interleaved (re, im)     */
 } trsm_dtype_t;
 
 /*
  * Solve L X = alpha B in place (B <- X).
- *   dtype  TRSM_R32F, TRSM_R64F or TRSM_C64F.
+ *   dtype  TRSM_R32F, TRSM_R64F, TRSM_C64F or TRSM_C32F.
  *   m, n   rows of B (= order of L) and columns of B; m, n >= 0.
- *   alpha  host pointer to one float / double / double[2] (re, im).
+ *   alpha  host pointer to one float / double / double[2] (re, im) /
+ *          float[2] (re, im), by dtype.
  *   A      device pointer, m x m, lda >= max(1, m).
  *   B      device pointer, m x n, ldb >= max(1, m); overwritten with X.
  * Quick returns: m == 0 or n == 0 does nothing; alpha == 0 sets B = 0
@@ -82,7 +85,7 @@ trsm_status_t trsm_lln(trsm_dtype_t dtype, int64_t m, int64_t n, const void *alp
 /*
  * Strided batch of independent solves (batched TRSM is named as future work
  * in section 6 of the pages): problem p uses A + p*strideA and B + p*strideB
- * (strides in elements of dtype; complex elements for TRSM_C64F) and the
+ * (strides in elements of dtype; complex elements for the complex types) and the
  * common alpha.  strideA >= lda*m and strideB >= ldb*n are not required,
  * but problems must not overlap in B.  batch == 0 is a quick return,
  * batch < 0 is INVALID_VALUE.  m <= 64 launches one grid over all problems;

@@ -52,8 +52,11 @@ class OracleLib:
         lib.oracle_lln_d_batched.argtypes = [i64, i64, dbl, vp, i64, i64, vp, i64, i64, i64]
         lib.oracle_lln_s_batched.argtypes = [i64, i64, flt, vp, i64, i64, vp, i64, i64, i64]
         lib.oracle_lln_z_batched.argtypes = [i64, i64, dbl, dbl, vp, i64, i64, vp, i64, i64, i64]
+        lib.oracle_lln_c.argtypes = [i64, i64, flt, flt, vp, i64, vp, i64]
+        lib.oracle_lln_c_batched.argtypes = [i64, i64, flt, flt, vp, i64, i64, vp, i64, i64, i64]
         for f in ("oracle_lln_d", "oracle_lln_d_rowdot", "oracle_lln_s", "oracle_lln_z",
-                  "oracle_lln_d_batched", "oracle_lln_s_batched", "oracle_lln_z_batched"):
+                  "oracle_lln_c", "oracle_lln_d_batched", "oracle_lln_s_batched",
+                  "oracle_lln_z_batched", "oracle_lln_c_batched"):
             getattr(lib, f).restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -66,7 +69,7 @@ class OracleLib:
         """Return X with L X = alpha B (a copy of B solved in place).
 
         L: m x m, B: m x n, column-major (or any layout: copied to Fortran
-        order), dtype float32, float64 or complex128.  Only the lower
+        order), dtype float32, float64, complex64 or complex128.  Only the lower
         triangle of L is read."""
         m = L.shape[0]
         if L.shape != (m, m) or B.shape[0] != m or L.dtype != B.dtype:
@@ -86,6 +89,9 @@ class OracleLib:
         elif L.dtype == np.complex128:
             a = complex(alpha)
             rc = lib.oracle_lln_z(m, n, a.real, a.imag, L.ctypes.data, lda, X.ctypes.data, ldx)
+        elif L.dtype == np.complex64:
+            a = complex(alpha)
+            rc = lib.oracle_lln_c(m, n, a.real, a.imag, L.ctypes.data, lda, X.ctypes.data, ldx)
         else:
             raise TypeError(f"unsupported dtype {L.dtype}")
         if rc != 0:
@@ -111,6 +117,10 @@ class OracleLib:
         elif L.dtype == np.complex128:
             a = complex(alpha)
             rc = lib.oracle_lln_z_batched(m, n, a.real, a.imag, Lc.ctypes.data, ld, sA,
+                                          Xc.ctypes.data, ld, sB, batch)
+        elif L.dtype == np.complex64:
+            a = complex(alpha)
+            rc = lib.oracle_lln_c_batched(m, n, a.real, a.imag, Lc.ctypes.data, ld, sA,
                                           Xc.ctypes.data, ld, sB, batch)
         else:
             raise TypeError(f"unsupported dtype {L.dtype}")

@@ -27,7 +27,8 @@
  *   - alpha == 0 sets X = 0 and does not read A;
  *   - no singularity check: a zero diagonal yields Inf/NaN.
  *
- * Complex data are interleaved (re, im) pairs of doubles.  The complex
+ * Complex data are interleaved (re, im) pairs of doubles (_z) or of floats
+ * (_c, complex fp32, computed in float: the operand precision).  The complex
  * arithmetic is written out in real operations:
  *   (a+bi)(c+di) = (ac - bd) + (ad + bc)i,
  *   (a+bi)/(c+0i) = a/c + (b/c)i                          (imag(divisor) == 0),
@@ -176,8 +177,60 @@ int oracle_lln_z(int64_t m, int64_t n, double alpha_re, double alpha_im,
     return 0;
 }
 
+/* ---- complex fp32, interleaved (re, im) floats ----------------------- */
+
+static void solve_column_c(int64_t m, float ar, float ai, const float *A,
+                           int64_t lda, float *b)
+{
+    int64_t i, k;
+    if (ar == 0.0f && ai == 0.0f) {
+        for (i = 0; i < 2 * m; ++i) b[i] = 0.0f;
+        return;
+    }
+    for (i = 0; i < m; ++i) {
+        float br = b[2 * i], bi = b[2 * i + 1];
+        b[2 * i]     = ar * br - ai * bi;
+        b[2 * i + 1] = ar * bi + ai * br;
+    }
+    for (k = 0; k < m; ++k) {
+        const float *lk = A + 2 * k * lda;
+        float dr = lk[2 * k], di = lk[2 * k + 1];
+        float br = b[2 * k], bi = b[2 * k + 1];
+        float xr, xi;
+        if (di == 0.0f) {
+            xr = br / dr;
+            xi = bi / dr;
+        } else {
+            float den = dr * dr + di * di;
+            xr = (br * dr + bi * di) / den;
+            xi = (bi * dr - br * di) / den;
+        }
+        b[2 * k] = xr;
+        b[2 * k + 1] = xi;
+        for (i = k + 1; i < m; ++i) {
+            float lr = lk[2 * i], li = lk[2 * i + 1];
+            float pr = lr * xr - li * xi;
+            float pi = lr * xi + li * xr;
+            b[2 * i]     = b[2 * i] - pr;
+            b[2 * i + 1] = b[2 * i + 1] - pi;
+        }
+    }
+}
+
+int oracle_lln_c(int64_t m, int64_t n, float alpha_re, float alpha_im,
+                 const float *A, int64_t lda, float *B, int64_t ldb)
+{
+    int64_t j;
+    if (m < 0 || n < 0 || lda < (m > 1 ? m : 1) || ldb < (m > 1 ? m : 1))
+        return 1;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (j = 0; j < n; ++j)
+        solve_column_c(m, alpha_re, alpha_im, A, lda, B + 2 * j * ldb);
+    return 0;
+}
+
 /* ---- strided batches: problem p at A + p*strideA, B + p*strideB ------- */
-/* Strides are in elements of the data type (complex elements for _z). */
+/* Strides are in elements of the data type (complex elements for _z, _c). */
 
 int oracle_lln_d_batched(int64_t m, int64_t n, double alpha, const double *A,
                          int64_t lda, int64_t strideA, double *B, int64_t ldb,
@@ -224,6 +277,23 @@ int oracle_lln_z_batched(int64_t m, int64_t n, double alpha_re,
     for (p = 0; p < batch; ++p)
         for (j = 0; j < n; ++j)
             solve_column_z(m, alpha_re, alpha_im, A + 2 * p * strideA, lda,
+                           B + 2 * p * strideB + 2 * j * ldb);
+    return 0;
+}
+
+int oracle_lln_c_batched(int64_t m, int64_t n, float alpha_re,
+                         float alpha_im, const float *A, int64_t lda,
+                         int64_t strideA, float *B, int64_t ldb,
+                         int64_t strideB, int64_t batch)
+{
+    int64_t p, j;
+    if (m < 0 || n < 0 || batch < 0 || lda < (m > 1 ? m : 1) ||
+        ldb < (m > 1 ? m : 1))
+        return 1;
+    #pragma omp parallel for schedule(dynamic, 1) private(j)
+    for (p = 0; p < batch; ++p)
+        for (j = 0; j < n; ++j)
+            solve_column_c(m, alpha_re, alpha_im, A + 2 * p * strideA, lda,
                            B + 2 * p * strideB + 2 * j * ldb);
     return 0;
 }

@@ -5,13 +5,15 @@ from __future__ import annotations
 
 import numpy as np
 
-TOL = {"f32": 1e-4, "f64": 1e-12, "c64": 1e-12}   # normwise relative error vs the oracle
-NP = {"f32": np.float32, "f64": np.float64, "c64": np.complex128}
+TOL = {"f32": 1e-4, "f64": 1e-12, "c64": 1e-12, "c32": 1e-4}   # normwise relative error vs the oracle
+NP = {"f32": np.float32, "f64": np.float64, "c64": np.complex128, "c32": np.complex64}
+CPLX = ("c64", "c32")
 
 
 def torch_dtype(dtype):
     import torch
-    return {"f32": torch.float32, "f64": torch.float64, "c64": torch.complex128}[dtype]
+    return {"f32": torch.float32, "f64": torch.float64, "c64": torch.complex128,
+            "c32": torch.complex64}[dtype]
 
 
 def ld_of(a):

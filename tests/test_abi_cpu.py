@@ -61,12 +61,12 @@ FAKE = 0x1000  # never dereferenced: every call below returns before any HIP cal
 
 
 def call(T, dtype=1, m=4, n=3, alpha=1.0, A=FAKE, lda=4, B=FAKE, ldb=4):
-    al = T.alpha_buffer(dtype if dtype in (0, 1, 2) else 1, alpha)
+    al = T.alpha_buffer(dtype if dtype in (0, 1, 2, 3) else 1, alpha)
     return T.lib.trsm_lln(dtype, m, n, ctypes.addressof(al), A, lda, B, ldb, None)
 
 
 @pytest.mark.parametrize("kw", [
-    dict(dtype=3), dict(dtype=-1), dict(m=-1), dict(n=-2), dict(lda=3), dict(ldb=3),
+    dict(dtype=4), dict(dtype=-1), dict(m=-1), dict(n=-2), dict(lda=3), dict(ldb=3),
     dict(m=0, lda=0), dict(A=None), dict(B=None), dict(m=5, lda=4, ldb=5), dict(m=5, lda=5, ldb=4),
 ])
 def test_invalid_arguments(T, kw):

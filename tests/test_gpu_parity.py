@@ -20,12 +20,12 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import TOL, from_dev, ld_of, max_problem_nrel, nrel, to_dev, torch_dtype
+from gpu_util import CPLX, TOL, from_dev, ld_of, max_problem_nrel, nrel, to_dev, torch_dtype
 from trsm_inputs import CONFIGS, make_config, make_problem, small_integer_rhs, unit_bidiagonal_minus_one
 
 pytestmark = pytest.mark.gpu
 
-SANITY = {"f32": 1e-5, "f64": 1e-13, "c64": 1e-13}
+SANITY = {"f32": 1e-5, "f64": 1e-13, "c64": 1e-13, "c32": 1e-5}
 
 
 @pytest.fixture(scope="module")
@@ -109,31 +109,31 @@ EDGE_M = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129]
 EDGE_N = [1, 5, 64, 65, 130]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_regime_edges(T, dtype):
     worst = 0.0
     for m in EDGE_M:
         for n in EDGE_N:
             L, B = make_problem(dtype, m, n, seed=1000 + 7 * m + n)
-            a = 0.5 - 0.25j if dtype == "c64" else 0.5
+            a = 0.5 - 0.25j if dtype in CPLX else 0.5
             X = solve_gpu(T, L, B, a)
             worst = max(worst, check(dtype, X, oracle.solve(L, B, a), f"{dtype} m={m} n={n}"))
     print(f"{dtype} regime edges: worst error {worst:.2e}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("ib", [64, 128, 256, 512, 1024])
 def test_every_block_size_ragged(T, dtype, ib):
     """m = 1000 is a multiple of no candidate block size (below 1024 it is
     one ragged block); n = 257 is ragged against the GEMM tiles."""
     m, n = 1000, 257
     L, B = make_problem(dtype, m, n, seed=ib)
-    a = 0.75 + 0.5j if dtype == "c64" else 0.75
+    a = 0.75 + 0.5j if dtype in CPLX else 0.75
     X = solve_gpu(T, L, B, a, ib=ib)
     check(dtype, X, oracle.solve(L, B, a), f"{dtype} ib={ib}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("schedule", ["left", "right"])
 @pytest.mark.parametrize("ib", [128, 256])
 def test_both_phase2_schedules(T, dtype, schedule, ib, monkeypatch):
@@ -144,12 +144,12 @@ def test_both_phase2_schedules(T, dtype, schedule, ib, monkeypatch):
     monkeypatch.setenv("TRSM_SCHEDULE", schedule)
     m, n = 1000, 257
     L, B = make_problem(dtype, m, n, seed=7 + ib)
-    a = -1.25 + 0.5j if dtype == "c64" else -1.25
+    a = -1.25 + 0.5j if dtype in CPLX else -1.25
     X = solve_gpu(T, L, B, a, ib=ib)
     check(dtype, X, oracle.solve(L, B, a), f"{dtype} {schedule} ib={ib}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_m_4097_narrow(T, dtype):
     m, n = 4097, 19
     L, B = make_problem(dtype, m, n, seed=4097)
@@ -157,7 +157,7 @@ def test_m_4097_narrow(T, dtype):
     check(dtype, X, oracle.solve(L, B, 1.0), f"{dtype} m=4097")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("m,n", [(50, 40), (700, 90)])
 def test_padding_and_poisoned_upper_triangle(T, dtype, m, n):
     """A's strict upper triangle and its padding rows hold NaN and must not
@@ -174,7 +174,7 @@ def test_padding_and_poisoned_upper_triangle(T, dtype, m, n):
     check(dtype, full[:m], oracle.solve(Lz, np.asfortranarray(B), 1.0), f"{dtype} padded")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_force_blocked_small_sizes(T, dtype):
     for m in (1, 17, 64):
         L, B = make_problem(dtype, m, 33, seed=m)
@@ -184,11 +184,11 @@ def test_force_blocked_small_sizes(T, dtype):
 
 # ---- batches -----------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("batch,m,n", [(1, 64, 64), (7, 33, 70), (7, 64, 64), (3, 150, 20)])
 def test_batched(T, dtype, batch, m, n):
     L, B = make_problem(dtype, m, n, seed=batch * 100 + m, batch=batch)
-    a = 0.5 - 0.25j if dtype == "c64" else -0.5
+    a = 0.5 - 0.25j if dtype in CPLX else -0.5
     Ad, Bd = to_dev(L), to_dev(B)
     T.trsm_lln_strided_batched(Ad, Bd, a)
     sync()
@@ -200,7 +200,7 @@ def test_batched(T, dtype, batch, m, n):
 
 # ---- special values and exact cases ------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("m", [40, 300])
 def test_alpha_zero_zeroes_B_without_reading_A(T, dtype, m):
     import torch
@@ -212,7 +212,7 @@ def test_alpha_zero_zeroes_B_without_reading_A(T, dtype, m):
     assert torch.all(Bd == 0).item()
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("m,ib", [(64, 0), (600, 128), (1000, 256)])
 def test_bidiagonal_exact(T, dtype, m, ib):
     """Unit bidiagonal L with -1 below the diagonal: X is the running sum of
@@ -224,7 +224,7 @@ def test_bidiagonal_exact(T, dtype, m, ib):
     assert np.array_equal(X, np.cumsum(B, axis=0)), f"{dtype} m={m}"
 
 
-@pytest.mark.parametrize("dtype", ["f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
 def test_deterministic(T, dtype):
     L, B = make_problem(dtype, 900, 300, seed=5)
     X1 = solve_gpu(T, L, B, 1.0)
@@ -232,7 +232,7 @@ def test_deterministic(T, dtype):
     assert np.array_equal(X1, X2)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_error_scale_vs_pages_table2(T, dtype):
     """At m = n = 1024 the GPU-vs-oracle error is of the order the pages
     report against a vendor TRSM (Table 2), at most 10x that figure."""
@@ -278,14 +278,14 @@ def test_workspace_allocation_failure_leaves_B_untouched(T, monkeypatch):
 
 # ---- the streaming batched kernel (>= 2 tasks per CU, fp64 / complex) -------
 
-@pytest.mark.parametrize("dtype", ["f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
 @pytest.mark.parametrize("batch,m,n", [(600, 64, 64), (600, 1, 64), (600, 17, 5), (520, 33, 100),
                                        (2100, 64, 64), (300, 48, 130)])
 def test_batched_streaming(T, dtype, batch, m, n):
     """Enough tasks (problem x 64-column group) for the persistent streaming
     kernel; ragged m, several column groups, more tasks than waves."""
     L, B = make_problem(dtype, m, n, seed=batch + 7 * m + n, batch=batch)
-    a = 0.5 - 0.25j if dtype == "c64" else -0.75
+    a = 0.5 - 0.25j if dtype in CPLX else -0.75
     Ad, Bd = to_dev(L), to_dev(B)
     T.trsm_lln_strided_batched(Ad, Bd, a)
     sync()
@@ -295,7 +295,7 @@ def test_batched_streaming(T, dtype, batch, m, n):
     assert e <= TOL[dtype] and e <= SANITY[dtype], e
 
 
-@pytest.mark.parametrize("dtype", ["f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
 def test_batched_streaming_padded_nan_upper(T, dtype):
     """Padded leading dimensions, a NaN strict upper triangle and NaN padding
     in A; B's padding rows must stay untouched."""
@@ -315,7 +315,7 @@ def test_batched_streaming_padded_nan_upper(T, dtype):
     assert e <= TOL[dtype] and e <= SANITY[dtype], e
 
 
-@pytest.mark.parametrize("dtype", ["f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
 def test_batched_streaming_bidiagonal_exact(T, dtype):
     """Unit bidiagonal L with -1 below the diagonal on every problem: X is the
     running column sum of integer B, exact on the streaming path."""

@@ -22,7 +22,8 @@ from trsm_inputs import make_problem
 
 pytestmark = pytest.mark.gpu
 
-U = {"f32": 2.0 ** -24, "f64": 2.0 ** -53, "c64": 2.0 ** -53}
+U = {"f32": 2.0 ** -24, "f64": 2.0 ** -53, "c64": 2.0 ** -53, "c32": 2.0 ** -24}
+CPLX = ("c64", "c32")
 
 
 @pytest.fixture(scope="module")
@@ -34,7 +35,7 @@ def T():
 
 
 def rand(dtype, rows, cols, rng, ld=None):
-    if dtype == "c64":
+    if dtype in CPLX:
         a = rng.uniform(-1, 1, (rows, cols)) + 1j * rng.uniform(-1, 1, (rows, cols))
     else:
         a = rng.uniform(-1, 1, (rows, cols))
@@ -64,7 +65,7 @@ def gemm_case(T, dtype, M, N, K, beta, gamma, *, seed=0, ldpad=0, split=0, a_low
     if split:
         D = D.copy()
         D[:split] = from_dev(D2d)[:split]
-    wide = np.complex128 if dtype == "c64" else np.float64
+    wide = np.complex128 if dtype in CPLX else np.float64
     A64, B64, C64 = A.astype(wide), Bm.astype(wide), C.astype(wide)
     ref = gamma * (A64 @ B64) + (beta * C64 if beta != 0 else 0)
     scale = abs(gamma) * (np.abs(A64) @ np.abs(B64)) + (abs(beta) * np.abs(C64) if beta != 0 else 0)
@@ -86,44 +87,44 @@ def rand_like_ld(a, ld):
 SHAPES = [(1, 1, 1), (17, 33, 5), (130, 129, 37), (64, 64, 64), (200, 70, 257), (513, 300, 48)]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_gemm_ragged_shapes(T, dtype):
     for i, (M, N, K) in enumerate(SHAPES):
         for beta, gamma in [(0.0, 1.0), (1.0, -1.0), (0.5, -1.0), (-2.0, 0.75)]:
-            if dtype == "c64":
+            if dtype in CPLX:
                 beta, gamma = complex(beta, 0.25 if beta else 0.0), complex(gamma, -0.5)
             gemm_case(T, dtype, M, N, K, beta, gamma, seed=i)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_gemm_large_tile_path(T, dtype):
     """Enough tiles (>= 1024) to take the large macro tile (fp64 128 x 64,
     complex 64 x 128), with a ragged K tile and odd leading dimensions
     (unaligned 16-byte loads)."""
-    M = 1450 if dtype == "c64" else 2900
+    M = 1450 if dtype in CPLX else 2900
     gemm_case(T, dtype, M, 2900, 45, 1.0, -1.0, seed=3)
     gemm_case(T, dtype, M, 2900, 40, 0.0, 1.0, seed=4, ldpad=3)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_gemm_split_routing(T, dtype):
     for split in (16, 37, 100):
         gemm_case(T, dtype, 300, 90, 64, 1.0, -1.0, seed=split, split=split)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_gemm_triangular(T, dtype):
     for M in (64, 100, 256, 300):
         gemm_case(T, dtype, M, 150, M, 0.0, 0.5, seed=M, a_lower=True)
 
 
-@pytest.mark.parametrize("dtype", ["f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
 def test_gemm_k_zero_and_gamma_zero(T, dtype):
     gemm_case(T, dtype, 50, 40, 0, 1.5, -1.0, seed=1)
     gemm_case(T, dtype, 50, 40, 30, 1.5, 0.0, seed=2)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("ib", [64, 128, 256, 512, 1024])
 def test_diag_inv_vs_oracle_identity_solve(T, dtype, ib):
     import torch
@@ -131,11 +132,12 @@ def test_diag_inv_vs_oracle_identity_solve(T, dtype, ib):
     L, _ = make_problem(dtype, m, 1, seed=ib)
     nb = (m + ib - 1) // ib
     W = torch.full((nb * ib * ib,), float("nan"), dtype={"f32": torch.float32, "f64": torch.float64,
-                                                         "c64": torch.complex128}[dtype], device="cuda")
+                                                         "c64": torch.complex128, "c32": torch.complex64}[dtype],
+                    device="cuda")
     T.trsm_kernel_diag_inv(to_dev(L), W, ib)
     torch.cuda.synchronize()
     Wh = from_dev(W)
-    tol = 1e-5 if dtype == "f32" else 1e-13
+    tol = 1e-5 if dtype in ("f32", "c32") else 1e-13
     for t in range(nb):
         r0 = t * ib
         bs = min(ib, m - r0)

@@ -45,9 +45,11 @@ from trsm_inputs import (CONFIGS, diagonal, identity, make_config, make_problem,
                          small_integer_rhs, unit_bidiagonal_minus_one)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-DTYPES = ["f32", "f64", "c64"]
-NP = {"f32": np.float32, "f64": np.float64, "c64": np.complex128}
-UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "f64": 2.0 ** -53, "c64": 2.0 ** -53}
+DTYPES = ["f32", "f64", "c64", "c32"]
+NP = {"f32": np.float32, "f64": np.float64, "c64": np.complex128, "c32": np.complex64}
+UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "f64": 2.0 ** -53, "c64": 2.0 ** -53, "c32": 2.0 ** -24}
+CPLX = ("c64", "c32")
+SINGLE = ("f32", "c32")
 
 
 def nrel(X, Xref):
@@ -73,7 +75,7 @@ def bits_equal(a, b):
 def check_identity(orc, dtype):
     for m, n in [(1, 1), (7, 3), (64, 64), (130, 5)]:
         B = small_integer_rhs(m, n, dtype, seed=m * 31 + n)
-        alphas = [1.0, 0.5, -2.0] + ([0.5 - 0.25j, -1j] if dtype == "c64" else [])
+        alphas = [1.0, 0.5, -2.0] + ([0.5 - 0.25j, -1j] if dtype in CPLX else [])
         for a in alphas:
             X = orc.solve(identity(m, dtype), B, a)
             expect = (np.asarray(a, dtype=NP[dtype]) * B).astype(NP[dtype])
@@ -86,28 +88,28 @@ def check_diagonal(orc, dtype):
     # powers of two: every step is exact
     d = rng.choice([0.5, 1.0, 2.0, 4.0, -2.0, -0.25], size=m)
     B = small_integer_rhs(m, n, dtype, seed=3)
-    for a in [1.0, -0.5] + ([0.5 - 0.25j] if dtype == "c64" else []):
+    for a in [1.0, -0.5] + ([0.5 - 0.25j] if dtype in CPLX else []):
         X = orc.solve(diagonal(d, dtype), B, a)
         aB = np.asarray(a, dtype=NP[dtype]) * B
-        if dtype == "c64":
+        if dtype in CPLX:
             expect = aB.real / d[:, None] + 1j * (aB.imag / d[:, None])
         else:
             expect = aB / d[:, None].astype(NP[dtype])
         assert bits_equal(X, np.asfortranarray(expect.astype(NP[dtype]))), (dtype, a)
     # general diagonal: alpha*b rounded, then one correctly rounded division
-    d = rng.uniform(1.0, 2.0, m).astype(np.float32 if dtype == "f32" else np.float64)
+    d = rng.uniform(1.0, 2.0, m).astype(np.float32 if dtype in SINGLE else np.float64)
     _, Bg = make_problem(dtype, m, n, seed=11)
     for a in [1.0, 0.7]:
         X = orc.solve(diagonal(d, dtype), Bg, a)
         aB = (np.asarray(a, dtype=NP[dtype]) * Bg).astype(NP[dtype])
-        if dtype == "c64":
+        if dtype in CPLX:
             expect = aB.real / d[:, None] + 1j * (aB.imag / d[:, None])
         else:
             expect = aB / d[:, None]
         assert bits_equal(X, np.asfortranarray(expect.astype(NP[dtype]))), (dtype, a)
-    if dtype == "c64":
+    if dtype in CPLX:
         # complex (non-real) diagonal: compare with numpy's complex division
-        dz = rng.uniform(1, 2, m) + 1j * rng.uniform(-1, 1, m)
+        dz = (rng.uniform(1, 2, m) + 1j * rng.uniform(-1, 1, m)).astype(NP[dtype])
         X = orc.solve(np.asfortranarray(np.diag(dz)), Bg, 1.0)
         expect = Bg / dz[:, None]
         err = np.abs(X - expect) / np.abs(expect)
@@ -121,7 +123,7 @@ def check_bidiagonal(orc, dtype):
     for m, n in [(1, 3), (2, 2), (65, 9), (300, 4)]:
         L = unit_bidiagonal_minus_one(m, dtype)
         B = small_integer_rhs(m, n, dtype, seed=m + 5)
-        for a in [1.0, 2.0] + ([1j] if dtype == "c64" else []):
+        for a in [1.0, 2.0] + ([1j] if dtype in CPLX else []):
             X = orc.solve(L, B, a)
             expect = np.asarray(a, dtype=NP[dtype]) * np.cumsum(B, axis=0)
             assert bits_equal(X, np.asfortranarray(expect.astype(NP[dtype]))), (dtype, m, a)
@@ -155,7 +157,7 @@ def exact_residual_is_zero(L, X, B, alpha):
 
 def random_integer_lower(m, dtype, rng, diag_choices):
     d = rng.choice(diag_choices, size=m)
-    if dtype == "c64":
+    if dtype in CPLX:
         off = rng.integers(-3, 4, (m, m)) + 1j * rng.integers(-3, 4, (m, m))
     else:
         off = rng.integers(-3, 4, (m, m))
@@ -166,11 +168,11 @@ def random_integer_lower(m, dtype, rng, diag_choices):
 def check_exact_dyadic(orc, dtype):
     rng = np.random.default_rng(2024)
     for trial in range(12):
-        m = int(rng.integers(1, 6 if dtype != "f32" else 4))
+        m = int(rng.integers(1, 6 if dtype not in SINGLE else 4))
         n = int(rng.integers(1, 5))
         L = random_integer_lower(m, dtype, rng, [1.0, -1.0, 2.0, -2.0, 4.0])
         B = small_integer_rhs(m, n, dtype, seed=trial)
-        for a in [1.0, -0.5] + ([0.5 + 0.5j] if dtype == "c64" else []):
+        for a in [1.0, -0.5] + ([0.5 + 0.5j] if dtype in CPLX else []):
             X = orc.solve(L, B, a)
             assert exact_residual_is_zero(L, X, B, a), (dtype, trial, a, L, B, X)
 
@@ -215,11 +217,11 @@ def exact_solution(L, B, alpha):
 def check_scipy(orc, dtype):
     """scipy's LAPACK trtrs (solve_triangular) and BLAS trsm as independent
     implementations of the same operation."""
-    tol = {"f32": 5e-6, "f64": 1e-14, "c64": 1e-14}[dtype]
+    tol = {"f32": 5e-6, "f64": 1e-14, "c64": 1e-14, "c32": 5e-6}[dtype]
     for (m, n, a) in [(64, 64, 1.0), (97, 33, 0.5), (200, 3, -1.5)] + (
-            [(50, 20, 0.5 - 0.25j)] if dtype == "c64" else []):
+            [(50, 20, 0.5 - 0.25j)] if dtype in CPLX else []):
         L, B = make_problem(dtype, m, n, seed=m * n)
-        if dtype == "c64":
+        if dtype in CPLX:
             # make the diagonal genuinely complex so the complex division is exercised
             idx = np.arange(m)
             L = np.array(L, order="F")
@@ -228,7 +230,7 @@ def check_scipy(orc, dtype):
         aB = (np.asarray(a, dtype=NP[dtype]) * B).astype(NP[dtype])
         ref = sla.solve_triangular(np.array(L), aB, lower=True)
         assert nrel(X, ref) < tol, (dtype, m, n, a, nrel(X, ref))
-        trsm = {"f32": sblas.strsm, "f64": sblas.dtrsm, "c64": sblas.ztrsm}[dtype]
+        trsm = {"f32": sblas.strsm, "f64": sblas.dtrsm, "c64": sblas.ztrsm, "c32": sblas.ctrsm}[dtype]
         ref2 = trsm(a, np.array(L, order="F"), np.array(B, order="F"), side=0, lower=1,
                     trans_a=0, diag=0)
         assert nrel(X, ref2) < tol, (dtype, m, n, a, nrel(X, ref2))
@@ -236,7 +238,7 @@ def check_scipy(orc, dtype):
 
 def check_batched_matches_single(orc, dtype):
     L, B = make_problem(dtype, 23, 6, seed=99, batch=5)
-    a = 0.5 - 0.25j if dtype == "c64" else 0.5
+    a = 0.5 - 0.25j if dtype in CPLX else 0.5
     Xb = orc.solve_batched(L, B, a)
     for p in range(5):
         assert bits_equal(np.asfortranarray(Xb[p]), orc.solve(L[p], B[p], a)), (dtype, p)
@@ -272,7 +274,7 @@ def test_brute_force_non_dyadic(orc, dtype):
         n = int(rng.integers(1, 5))
         L = random_integer_lower(m, dtype, rng, [3.0, 5.0, -3.0, 7.0, 1.0])
         B = small_integer_rhs(m, n, dtype, seed=100 + trial)
-        a = 0.75 - 0.5j if dtype == "c64" else 0.75
+        a = 0.75 - 0.5j if dtype in CPLX else 0.75
         X = orc.solve(L, B, a)
         Xe = exact_solution(L, B, a)
         assert nrel(X, Xe) <= 8 * m * u, (dtype, trial, nrel(X, Xe))
@@ -295,7 +297,7 @@ def test_loop_order_invariance(orc):
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_alpha_scaling(orc, dtype):
     L, B = make_problem(dtype, 80, 10, seed=8)
-    a = 0.3 + 0.2j if dtype == "c64" else 0.3
+    a = 0.3 + 0.2j if dtype in CPLX else 0.3
     X1 = orc.solve(L, B, 1.0)
     Xa = orc.solve(L, B, a)
     assert nrel(Xa, np.asarray(a) * X1) < 20 * UNIT_ROUNDOFF[dtype]
@@ -344,7 +346,7 @@ def test_residual_bound_configs(orc, dtype):
             assert np.linalg.norm(R) / den <= 10 * cfg.m * u, (cfg.name, np.linalg.norm(R) / den)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_error_scale_vs_pages_table2(orc, dtype):
     """Against an independent TRSM (scipy/LAPACK) at m = n = 1024 the oracle's
     normwise difference is of the order the pages report against a vendor
@@ -390,6 +392,16 @@ MUTANTS = [
     ("z_real_div", "solve_column_z", "xi = bi / dr;", "xi = bi * dr;"),
     ("z_swapped_parts", "solve_column_z", "double lr = lk[2 * i], li = lk[2 * i + 1];",
      "double li = lk[2 * i], lr = lk[2 * i + 1];"),
+    ("c_conj_product_im", "solve_column_c", "float pi = lr * xi + li * xr;",
+     "float pi = lr * xi - li * xr;"),
+    ("c_div_sign", "solve_column_c", "xi = (bi * dr - br * di) / den;",
+     "xi = (bi * dr + br * di) / den;"),
+    ("c_swapped_parts", "solve_column_c", "float lr = lk[2 * i], li = lk[2 * i + 1];",
+     "float li = lk[2 * i], lr = lk[2 * i + 1];"),
+    ("c_alpha_dropped_im", "solve_column_c", "b[2 * i + 1] = ar * bi + ai * br;",
+     "b[2 * i + 1] = ar * bi;"),
+    ("c_batched_stride", "oracle_lln_c_batched", "solve_column_c(m, alpha_re, alpha_im, A + 2 * p * strideA, lda,",
+     "solve_column_c(m, alpha_re, alpha_im, A + p * strideA, lda,"),
     ("batched_stride", "oracle_lln_d_batched", "solve_column_d(m, alpha, A + p * strideA, lda,",
      "solve_column_d(m, alpha, A, lda,"),
 ]

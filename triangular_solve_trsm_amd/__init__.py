@@ -13,7 +13,8 @@ kernels.  The functions carry the names of the C ABI (include/trsm.h):
 A and B are torch tensors on the GPU in column-major storage: for an m x n
 operand, stride(0) == 1 and stride(1) == ld >= m (``colmajor_empty`` makes
 one).  Batched operands are (batch, m, n) with strides (stride, 1, ld).
-Supported dtypes: torch.float32, torch.float64, torch.complex128.  B is
+Supported dtypes: torch.float32, torch.float64, torch.complex64,
+torch.complex128.  B is
 overwritten with X such that L X = alpha B, L the lower triangle of A.
 
 The library must have been built (``python triangular_solve_trsm_amd/build.py``
@@ -27,7 +28,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtrsm_amd.so")
 
-R32F, R64F, C64F = 0, 1, 2
+R32F, R64F, C64F, C32F = 0, 1, 2, 3
 STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "ALLOC_FAILED", 3: "HIP_ERROR", 4: "NOT_SUPPORTED"}
 IB_CHOICES = (64, 128, 256, 512, 1024)
 
@@ -94,19 +95,22 @@ lib = _load()
 
 def _dtype_code(t) -> int:
     import torch
-    code = {torch.float32: R32F, torch.float64: R64F, torch.complex128: C64F}.get(t.dtype)
+    code = {torch.float32: R32F, torch.float64: R64F, torch.complex128: C64F, torch.complex64: C32F}.get(t.dtype)
     if code is None:
-        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float64 or complex128")
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, float64, complex64 or complex128")
     return code
 
 
 def alpha_buffer(code: int, alpha):
-    """Host scalar in the layout the ABI expects (float / double / double[2])."""
+    """Host scalar in the layout the ABI expects (float / double / double[2] /
+    float[2])."""
     if code == R32F:
         return ctypes.c_float(float(alpha))
     if code == R64F:
         return ctypes.c_double(float(alpha))
     a = complex(alpha)
+    if code == C32F:
+        return (ctypes.c_float * 2)(a.real, a.imag)
     return (ctypes.c_double * 2)(a.real, a.imag)
 
 
@@ -196,10 +200,10 @@ def trsm_lln_strided_batched(A, B, alpha=1.0, *, stream=None):
 
 def trsm_lln_select_ib(dtype, m: int, n: int) -> int:
     """Block size of the offline table for (dtype, m, n); dtype is a torch
-    dtype or one of R32F / R64F / C64F."""
+    dtype or one of R32F / R64F / C64F / C32F."""
     if not isinstance(dtype, int):
         import torch
-        dtype = {torch.float32: R32F, torch.float64: R64F, torch.complex128: C64F}[dtype]
+        dtype = {torch.float32: R32F, torch.float64: R64F, torch.complex128: C64F, torch.complex64: C32F}[dtype]
     return int(lib.trsm_lln_select_ib(dtype, m, n))
 
 

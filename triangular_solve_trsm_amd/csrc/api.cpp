@@ -151,13 +151,19 @@ class LaunchTimer {
 
 // ---- argument handling --------------------------------------------------
 
-bool valid_dtype(int dt) { return dt == TRSM_R32F || dt == TRSM_R64F || dt == TRSM_C64F; }
+bool valid_dtype(int dt) {
+    return dt == TRSM_R32F || dt == TRSM_R64F || dt == TRSM_C64F || dt == TRSM_C32F;
+}
 
 Scalar read_alpha(int dt, const void *alpha) {
     Scalar s{0.0, 0.0};
     if (dt == TRSM_R32F) s.re = *static_cast<const float *>(alpha);
     else if (dt == TRSM_R64F) s.re = *static_cast<const double *>(alpha);
-    else {
+    else if (dt == TRSM_C32F) {
+        const float *a = static_cast<const float *>(alpha);
+        s.re = a[0];
+        s.im = a[1];
+    } else {
         const double *a = static_cast<const double *>(alpha);
         s.re = a[0];
         s.im = a[1];
@@ -215,7 +221,7 @@ bool use_left_looking(int dt, int64_t m, int64_t n, int ib, bool table_left) {
     if (e && std::strcmp(e, "left") == 0) return true;
     if (e && std::strcmp(e, "right") == 0) return false;
     if (!table_left) return false;
-    const int64_t rows = (dt == C64F ? 2 : 1) * (int64_t)(ib < m ? ib : m);  // real rows of an update
+    const int64_t rows = (dt == C64F || dt == C32F ? 2 : 1) * (int64_t)(ib < m ? ib : m);  // real rows
     return ((rows + 63) / 64) * ((n + 63) / 64) >= kLeftMinTiles;
 }
 

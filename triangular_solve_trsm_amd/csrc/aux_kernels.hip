@@ -68,6 +68,8 @@ hipError_t fill_zero_launch(int dtype, int64_t m, int64_t n, void *B, int64_t ld
         case R32F: return fill_t<float>(m, n, B, ldb, strideB, batch, stream);
         case R64F: return fill_t<double>(m, n, B, ldb, strideB, batch, stream);
         case C64F: return fill_t<cplx>(m, n, B, ldb, strideB, batch, stream);
+        // complex fp32 is 8 bytes: zero bits and a bit copy, as for fp64
+        case C32F: return fill_t<double>(m, n, B, ldb, strideB, batch, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -78,6 +80,7 @@ hipError_t copy_panel_launch(int dtype, int64_t rows, int64_t n, const void *src
         case R32F: return copy_t<float>(rows, n, src, lds, dst, ldd, stream);
         case R64F: return copy_t<double>(rows, n, src, lds, dst, ldd, stream);
         case C64F: return copy_t<cplx>(rows, n, src, lds, dst, ldd, stream);
+        case C32F: return copy_t<double>(rows, n, src, lds, dst, ldd, stream);
         default: return hipErrorInvalidValue;
     }
 }

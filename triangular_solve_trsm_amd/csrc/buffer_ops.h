@@ -3,6 +3,10 @@
 // control flow.  Internal to the library.
 #pragma once
 
+#include <type_traits>
+
+#include "trsm_internal.h"
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,7 +56,12 @@ __device__ __forceinline__ void ld_elems(__amdgpu_buffer_rsrc_t r, uint32_t off,
             // Bit-cast the whole vector to a vector of T and index that: a
             // bit cast of each u4v element on its own was compiled as a
             // repeat of element 0 (seen with hipcc for gfx950).
-            if constexpr (sizeof(T) == 4) {
+            if constexpr (std::is_same<T, cplx32>::value) {
+                typedef float f4t __attribute__((ext_vector_type(4)));
+                const f4t w = __builtin_bit_cast(f4t, v);
+                dst[q * 2] = cplx32{w[0], w[1]};
+                dst[q * 2 + 1] = cplx32{w[2], w[3]};
+            } else if constexpr (sizeof(T) == 4) {
                 typedef T v4t __attribute__((ext_vector_type(4)));
                 const v4t w = __builtin_bit_cast(v4t, v);
 #pragma unroll

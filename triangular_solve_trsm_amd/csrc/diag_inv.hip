@@ -61,6 +61,9 @@ __device__ __forceinline__ double bcast(double v, int src) {
 __device__ __forceinline__ cplx bcast(cplx v, int src) {
     return cplx{bcast(v.re, src), bcast(v.im, src)};
 }
+__device__ __forceinline__ cplx32 bcast(cplx32 v, int src) {
+    return cplx32{bcast(v.re, src), bcast(v.im, src)};
+}
 
 template <typename T> constexpr int words() { return sizeof(T) / 4; }
 
@@ -217,6 +220,7 @@ hipError_t launch_base(int dtype, int64_t m, const void *A, int64_t lda, void *W
         case R32F: return launch_r<float, 1, kBaseCols>(m, A, lda, W, ldw, st);
         case R64F: return launch_r<double, 1, kBaseCols>(m, A, lda, W, ldw, st);
         case C64F: return launch_r<cplx, 1, kBaseCols>(m, A, lda, W, ldw, st);
+        case C32F: return launch_r<cplx32, 1, kBaseCols>(m, A, lda, W, ldw, st);
         default: return hipErrorInvalidValue;
     }
 }

@@ -74,6 +74,8 @@ template <> struct GemmTraits<float> {
     // Row of a 16-row block fed by lane c of the A operand.  The f32 result
     // puts rows 4q .. 4q+3 in lane group q already.
     __device__ __forceinline__ static int a_row(int c) { return c; }
+    __device__ __forceinline__ static int a_crow(int) { return 0; }  // complex only
+    __device__ __forceinline__ static int a_ri(int) { return 0; }
 };
 template <> struct GemmTraits<double> {
     using R = double;
@@ -86,7 +88,13 @@ template <> struct GemmTraits<double> {
     // (checked on gfx950); feeding row 4(c%4) + c/4 as MFMA row c turns that
     // into rows 4q .. 4q+3.
     __device__ __forceinline__ static int a_row(int c) { return 4 * (c & 3) + (c >> 2); }
+    __device__ __forceinline__ static int a_crow(int) { return 0; }  // complex only
+    __device__ __forceinline__ static int a_ri(int) { return 0; }
 };
+// Complex types: real row c of a 16-row MFMA block stands for complex row
+// a_crow(c) of the block's 8, part a_ri(c) (0 re, 1 im), chosen so that
+// with the result layout a lane holds complex rows 2q (items 0, 1) and
+// 2q + 1 (items 2, 3) of lane group q.
 template <> struct GemmTraits<cplx> {
     using R = double;
     using Acc = d4;
@@ -95,6 +103,21 @@ template <> struct GemmTraits<cplx> {
         return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
     }
     __device__ __forceinline__ static int a_row(int c) { return c; }
+    // f64 result: row q + 4v in item v
+    __device__ __forceinline__ static int a_crow(int c) { return 2 * (c & 3) + (c >> 3); }
+    __device__ __forceinline__ static int a_ri(int c) { return (c >> 2) & 1; }
+};
+template <> struct GemmTraits<cplx32> {
+    using R = float;
+    using Acc = f4;
+    static constexpr bool kCplx = true;
+    __device__ __forceinline__ static Acc mfma(R a, R b, Acc c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static int a_row(int c) { return c; }
+    // f32 result: row 4q + v in item v
+    __device__ __forceinline__ static int a_crow(int c) { return c >> 1; }
+    __device__ __forceinline__ static int a_ri(int c) { return c & 1; }
 };
 
 template <typename T>
@@ -198,7 +221,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     // A tile: AK columns x AR rows of T (complex: complex rows and k).
     constexpr int AK = CPLX ? KT / 2 : KT;
     constexpr int AR = CPLX ? MT / 2 : MT;
-    constexpr int AU = CPLX ? 1 : VR;  // elements of T per 16-byte load
+    constexpr int AU = 16 / (int)sizeof(T);  // elements of T per 16-byte load
     constexpr int SA = AR + 4;         // row pitch (16-byte multiple)
     // Swizzle of the A tile.  Lane group q reads k rows [q*KPG, q*KPG + KPG)
     // of the tile, and with any 16-byte pitch those start 0 or 32 banks
@@ -258,17 +281,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         Acc acc[FM][FN];
         if (p.has_c) {
             if constexpr (CPLX) {
-                const cplx sc{p.sc.re, p.sc.im};
+                const T sc = Elem<T>::from(p.sc);
 #pragma unroll
                 for (int a = 0; a < FM; ++a) {
                     const int64_t cb = (i0 + wm * WM + a * 16) / 2 + 2 * q;  // complex rows cb, cb+1
 #pragma unroll
                     for (int b = 0; b < FN; ++b) {
                         const int64_t j = j0 + wn * WN + b * 16 + c16;
-                        cplx z0{0.0, 0.0}, z1{0.0, 0.0};
+                        T z0 = Elem<T>::zero(), z1 = Elem<T>::zero();
                         if (j < p.N) {
-                            if (cb < p.M) z0 = Elem<cplx>::mul(sc, pC[cb + j * p.ldc]);
-                            if (cb + 1 < p.M) z1 = Elem<cplx>::mul(sc, pC[cb + 1 + j * p.ldc]);
+                            if (cb < p.M) z0 = Elem<T>::mul(sc, pC[cb + j * p.ldc]);
+                            if (cb + 1 < p.M) z1 = Elem<T>::mul(sc, pC[cb + 1 + j * p.ldc]);
                         }
                         acc[a][b] = Acc{z0.re, z0.im, z1.re, z1.im};
                     }
@@ -386,8 +409,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         // 16-row block stands for complex row 2(t % 4) + t / 8 of the block's 8,
         // part (t / 4) % 2; with the f64 result layout (row q + 4v in item v) a
         // lane then holds complex rows 2q (items 0, 1) and 2q + 1 (items 2, 3).
-        const int a_crow = 2 * (c16 & 3) + (c16 >> 3);
-        const int a_ri = (c16 >> 2) & 1;
+        const int a_crow = CPLX ? Tr::a_crow(c16) : 0;
+        const int a_ri = CPLX ? Tr::a_ri(c16) : 0;
         const int a_row = Tr::a_row(c16);
 
         // Products of the K tile in LDS buffer buf.
@@ -414,9 +437,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
                 for (int a = 0; a < FM; ++a) {
                     if constexpr (CPLX) {
                         // real k = kb + e: complex k (kb + e) / 2, part e % 2 (kb even)
-                        const cplx z = As[buf][kb >> 1][((wm * WM + a * 16) / 2 + a_crow) ^ a_swz(kb >> 1)];
-                        af[a][0] = a_ri ? z.im : z.re;    // k part 0
-                        af[a][1] = a_ri ? z.re : -z.im;   // k part 1
+#pragma unroll
+                        for (int e2 = 0; e2 < CW / 2; ++e2) {
+                            const int kc = (kb >> 1) + e2;
+                            const T z = As[buf][kc][((wm * WM + a * 16) / 2 + a_crow) ^ a_swz(kc)];
+                            af[a][2 * e2] = a_ri ? z.im : z.re;       // k part 0
+                            af[a][2 * e2 + 1] = a_ri ? z.re : -z.im;  // k part 1
+                        }
                     } else {
 #pragma unroll
                         for (int e = 0; e < CW; ++e)
@@ -473,7 +500,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
 
         // ---- epilogue: D = gamma * acc, rows below `split` to D2 --------------
         if constexpr (CPLX) {
-            const cplx gamma{p.gamma.re, p.gamma.im};
+            const T gamma = Elem<T>::from(p.gamma);
 #pragma unroll
             for (int a = 0; a < FM; ++a) {
                 const int64_t cb = (i0 + wm * WM + a * 16) / 2 + 2 * q;
@@ -485,7 +512,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
                     for (int h = 0; h < 2; ++h) {
                         const int64_t ic = cb + h;
                         if (ic >= p.M) continue;
-                        const cplx out = Elem<cplx>::mul(gamma, cplx{acc[a][b][2 * h], acc[a][b][2 * h + 1]});
+                        const T out = Elem<T>::mul(gamma, T{acc[a][b][2 * h], acc[a][b][2 * h + 1]});
                         if (ic < p.split) pD2[ic + j * p.ldd2] = out;
                         else pD[ic + j * p.ldd] = out;
                     }
@@ -646,6 +673,7 @@ hipError_t gemm_launch(int dtype, const GemmDesc &g, hipStream_t stream) {
         case R32F: return launch_sized<float, 32>(g, stream);
         case R64F: return launch_sized<double, 16>(g, stream);
         case C64F: return launch_sized<cplx, 16>(g, stream);
+        case C32F: return launch_sized<cplx32, 32>(g, stream);
         default: return hipErrorInvalidValue;
     }
 }

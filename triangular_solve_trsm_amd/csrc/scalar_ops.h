@@ -1,4 +1,4 @@
-// Device arithmetic on the three element types (float, double, cplx).
+// Device arithmetic on the element types (float, double, cplx, cplx32).
 // Complex products are written out in real fused multiply-adds; no operand is
 // conjugated.
 #pragma once
@@ -66,6 +66,33 @@ template <> struct Elem<cplx> {
     // c ? a : b, part by part (keeps the values in registers)
     __device__ __forceinline__ static cplx sel(bool c, cplx a, cplx b) {
         return cplx{c ? a.re : b.re, c ? a.im : b.im};
+    }
+};
+
+template <> struct Elem<cplx32> {
+    using Real = float;
+    static constexpr int kDType = C32F;
+    __device__ __forceinline__ static cplx32 zero() { return cplx32{0.0f, 0.0f}; }
+    __device__ __forceinline__ static cplx32 one() { return cplx32{1.0f, 0.0f}; }
+    __device__ __forceinline__ static cplx32 from(Scalar s) { return cplx32{(float)s.re, (float)s.im}; }
+    __device__ __forceinline__ static cplx32 mul(cplx32 a, cplx32 b) {
+        return cplx32{__builtin_fmaf(a.re, b.re, -a.im * b.im),
+                      __builtin_fmaf(a.re, b.im, a.im * b.re)};
+    }
+    __device__ __forceinline__ static cplx32 msub(cplx32 b, cplx32 l, cplx32 x) {
+        float r = __builtin_fmaf(-l.re, x.re, b.re);
+        r = __builtin_fmaf(l.im, x.im, r);
+        float i = __builtin_fmaf(-l.re, x.im, b.im);
+        i = __builtin_fmaf(-l.im, x.re, i);
+        return cplx32{r, i};
+    }
+    __device__ __forceinline__ static cplx32 recip(cplx32 d) {
+        if (d.im == 0.0f) return cplx32{1.0f / d.re, 0.0f};
+        float den = d.re * d.re + d.im * d.im;
+        return cplx32{d.re / den, -d.im / den};
+    }
+    __device__ __forceinline__ static cplx32 sel(bool c, cplx32 a, cplx32 b) {
+        return cplx32{c ? a.re : b.re, c ? a.im : b.im};
     }
 };
 

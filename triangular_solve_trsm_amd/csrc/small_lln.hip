@@ -137,7 +137,8 @@ hipError_t small_lln_launch(int dtype, int m, int64_t n, Scalar alpha, const voi
                             int64_t lda, int64_t strideA, void *B, int64_t ldb,
                             int64_t strideB, int64_t batch, hipStream_t stream) {
     if (m < 1 || m > 64) return hipErrorInvalidValue;
-    // fp64 and complex fp64 run on the matrix cores (small_mfma.hip).
+    // fp64 and complex fp64 run on the matrix cores (small_mfma.hip); fp32
+    // and complex fp32 on the vector units here.
     if (dtype == R64F || dtype == C64F)
         return small_mfma_launch(dtype, m, n, alpha, A, lda, strideA, B, ldb, strideB, batch,
                                  stream);
@@ -145,6 +146,7 @@ hipError_t small_lln_launch(int dtype, int m, int64_t n, Scalar alpha, const voi
         case R32F: return launch_t<float>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, stream);
         case R64F: return launch_t<double>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, stream);
         case C64F: return launch_t<cplx>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, stream);
+        case C32F: return launch_t<cplx32>(m, n, alpha, A, lda, strideA, B, ldb, strideB, batch, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -13,11 +13,16 @@ namespace trsm {
 struct alignas(16) cplx {
     double re, im;
 };
+// Complex fp32: an interleaved (re, im) pair of floats, layout-compatible
+// with hipFloatComplex.
+struct alignas(8) cplx32 {
+    float re, im;
+};
 
-enum DType : int { R32F = 0, R64F = 1, C64F = 2 };
+enum DType : int { R32F = 0, R64F = 1, C64F = 2, C32F = 3 };
 
 inline size_t dtype_size(int dt) {
-    return dt == R32F ? 4 : dt == R64F ? 8 : 16;
+    return dt == R32F ? 4 : (dt == R64F || dt == C32F) ? 8 : 16;
 }
 
 // Scalars travel between host and device code as a pair of doubles

@@ -33,7 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 CANDIDATES = (64, 128, 256, 512, 1024)
-DTYPES = (("f32", "R32F"), ("f64", "R64F"), ("c64", "C64F"))
+DTYPES = (("f32", "R32F"), ("f64", "R64F"), ("c64", "C64F"), ("c32", "C32F"))
 DEFAULT_SIZES = (128, 256, 512, 1024, 2048, 4096, 8192, 16384)
 
 
@@ -82,7 +82,7 @@ def main():
             Ad = torch.from_numpy(np.ascontiguousarray(L.T)).cuda().T
             B0 = torch.from_numpy(np.ascontiguousarray(B.T)).cuda().T
             del L, B
-            alpha = 1.0 + 0j if dt == "c64" else 1.0
+            alpha = 1.0 + 0j if dt in ("c64", "c32") else 1.0
             row = {}
             for ib in CANDIDATES:
                 if ib > m:

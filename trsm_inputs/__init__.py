@@ -15,7 +15,8 @@ HSMA-TRSM, section 5.1 "Test Configuration"):
   diagonal, imaginary part 0), then the real and imaginary parts of B;
 * batched problems: the same draws with a leading batch axis on every array,
   whole arrays drawn in the order above;
-* fp32 problems are drawn in float64 and rounded to float32;
+* fp32 and complex-fp32 problems are drawn in float64 and rounded to
+  float32 parts;
 * storage is column-major per problem (element (i, j) at ``i + j*ld``).
 
 Off-diagonal magnitudes of at most 1/m (sqrt(2)/m for complex) against a
@@ -32,13 +33,14 @@ import numpy as np
 
 SEED_BASE = 20261201
 
-_NP_DTYPE = {"f32": np.float32, "f64": np.float64, "c64": np.complex128}
+_NP_DTYPE = {"f32": np.float32, "f64": np.float64, "c64": np.complex128, "c32": np.complex64}
+_COMPLEX = ("c64", "c32")
 
 
 @dataclass(frozen=True)
 class Config:
     name: str
-    dtype: str          # "f32" | "f64" | "c64"  (c64 = complex fp64)
+    dtype: str          # "f32" | "f64" | "c64" | "c32"  (complex fp64 / fp32)
     m: int
     n: int
     alpha: complex
@@ -52,7 +54,7 @@ class Config:
     @property
     def flops(self) -> float:
         """Counted flops: m^2 n (real), 4 m^2 n (complex), per problem times batch."""
-        f = float(self.m) * self.m * self.n * (4.0 if self.dtype == "c64" else 1.0)
+        f = float(self.m) * self.m * self.n * (4.0 if self.dtype in _COMPLEX else 1.0)
         return f * (self.batch or 1)
 
 
@@ -100,7 +102,7 @@ def make_problem(dtype: str, m: int, n: int, seed: int, *, batch: Optional[int] 
     shp_u = (m, m) if batch is None else (batch, m, m)
     shp_d = (m,) if batch is None else (batch, m)
     shp_b = (m, n) if batch is None else (batch, m, n)
-    if dtype == "c64":
+    if dtype in _COMPLEX:
         U = rng.uniform(-1.0, 1.0, shp_u) + 1j * rng.uniform(-1.0, 1.0, shp_u)
         d = rng.uniform(1.0, 2.0, shp_d).astype(np.complex128)
         Bv = rng.uniform(-1.0, 1.0, shp_b) + 1j * rng.uniform(-1.0, 1.0, shp_b)
@@ -127,7 +129,7 @@ def make_problem(dtype: str, m: int, n: int, seed: int, *, batch: Optional[int] 
 def make_config(cfg: Config, **kw):
     """(L, B, alpha) for one of CONFIGS, drawn with the config's seed."""
     L, B = make_problem(cfg.dtype, cfg.m, cfg.n, cfg.seed, batch=cfg.batch, **kw)
-    alpha = complex(cfg.alpha) if cfg.dtype == "c64" else float(np.real(cfg.alpha))
+    alpha = complex(cfg.alpha) if cfg.dtype in _COMPLEX else float(np.real(cfg.alpha))
     return L, B, alpha
 
 
@@ -152,7 +154,7 @@ def unit_bidiagonal_minus_one(m: int, dtype: str):
 def small_integer_rhs(m: int, n: int, dtype: str, seed: int, lo: int = -8, hi: int = 8):
     """Integer-valued B (real and imaginary parts for complex) in [lo, hi]."""
     rng = np.random.default_rng(seed)
-    if dtype == "c64":
+    if dtype in _COMPLEX:
         B = rng.integers(lo, hi + 1, (m, n)) + 1j * rng.integers(lo, hi + 1, (m, n))
     else:
         B = rng.integers(lo, hi + 1, (m, n))
