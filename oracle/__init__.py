@@ -54,9 +54,13 @@ class OracleLib:
         lib.oracle_lln_z_batched.argtypes = [i64, i64, dbl, dbl, vp, i64, i64, vp, i64, i64, i64]
         lib.oracle_lln_c.argtypes = [i64, i64, flt, flt, vp, i64, vp, i64]
         lib.oracle_lln_c_batched.argtypes = [i64, i64, flt, flt, vp, i64, i64, vp, i64, i64, i64]
+        ci = ctypes.c_int
+        lib.oracle_trsm_d.argtypes = [ci, ci, ci, ci, ci, i64, i64, dbl, dbl, vp, i64, vp, i64]
+        lib.oracle_trsm_s.argtypes = [ci, ci, ci, ci, ci, i64, i64, flt, flt, vp, i64, vp, i64]
         for f in ("oracle_lln_d", "oracle_lln_d_rowdot", "oracle_lln_s", "oracle_lln_z",
                   "oracle_lln_c", "oracle_lln_d_batched", "oracle_lln_s_batched",
-                  "oracle_lln_z_batched", "oracle_lln_c_batched"):
+                  "oracle_lln_z_batched", "oracle_lln_c_batched", "oracle_trsm_d",
+                  "oracle_trsm_s"):
             getattr(lib, f).restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -129,6 +133,35 @@ class OracleLib:
         return np.transpose(Xc, (0, 2, 1))
 
 
+    def trsm(self, side: str, uplo: str, trans: str, diag: str, A: np.ndarray, B: np.ndarray,
+             alpha=1.0) -> np.ndarray:
+        """General TRSM by its definition: op(A) X = alpha B (side 'L', A
+        m x m) or X op(A) = alpha B (side 'R', A n x n); uplo 'L'/'U' names
+        the triangle of A that is used, trans 'N'/'T'/'C' gives op(A) = A,
+        A^T or A^H, diag 'N'/'U' non-unit or unit (then the diagonal of A is
+        not read).  Returns X (a new array)."""
+        codes = ({"L": 0, "R": 1}[side], {"L": 0, "U": 1}[uplo], {"N": 0, "T": 1, "C": 2}[trans],
+                 {"N": 0, "U": 1}[diag])
+        m, n = B.shape
+        k = m if side == "L" else n
+        if A.shape != (k, k) or A.dtype != B.dtype:
+            raise ValueError("shape/dtype mismatch")
+        X = np.array(B, order="F", copy=True)
+        A, lda = _colmajor(A)
+        cplx = int(np.iscomplexobj(A))
+        a = complex(alpha)
+        if A.dtype in (np.float64, np.complex128):
+            f = self.lib.oracle_trsm_d
+        elif A.dtype in (np.float32, np.complex64):
+            f = self.lib.oracle_trsm_s
+        else:
+            raise TypeError(f"unsupported dtype {A.dtype}")
+        rc = f(*codes, cplx, m, n, a.real, a.imag, A.ctypes.data, lda, X.ctypes.data, max(m, 1))
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments")
+        return X
+
+
 _default = None
 
 
@@ -147,6 +180,10 @@ def num_threads() -> int:
 def solve(L, B, alpha=1.0, *, rowdot: bool = False):
     """Module-level shortcut for OracleLib.solve on the default build."""
     return _load().solve(L, B, alpha, rowdot=rowdot)
+
+
+def trsm(side, uplo, trans, diag, A, B, alpha=1.0):
+    return _load().trsm(side, uplo, trans, diag, A, B, alpha)
 
 
 def solve_batched(L, B, alpha=1.0):

@@ -298,6 +298,186 @@ int oracle_lln_c_batched(int64_t m, int64_t n, float alpha_re,
     return 0;
 }
 
+/* ---- every TRSM variant, by its definition ------------------------------
+ *
+ * The general BLAS TRSM (section 2.1 of the pages: op(A) X = alpha B, and its
+ * right-side form X op(A) = alpha B):
+ *   side  0: op(A) X = alpha B, A is m x m;  1: X op(A) = alpha B, A is n x n;
+ *   uplo  0: the lower triangle of A is used, 1: the upper;
+ *   trans 0: op(A) = A, 1: A^T, 2: A^H (conjugate transpose);
+ *   diag  0: non-unit, 1: unit diagonal (the diagonal of A is not read);
+ *   cplx  1: A and B hold interleaved complex values, 0: real values.
+ * Each right-hand side -- a column of B for side 0, a row of B for side 1 --
+ * is the solution y of a triangular system T y = alpha c, with T = op(A) for
+ * side 0 and T = op(A)^T for side 1 (x op(A) = alpha b is, entry by entry,
+ * sum_k x_k op(A)_kj = alpha b_j).  T is lower or upper triangular and is
+ * solved by substitution starting where its triangle starts:
+ *     y_i = (alpha c_i - sum_{j solved before i} T_ij y_j) / T_ii,
+ * the solved terms subtracted in the order they were solved.  The complex
+ * arithmetic is written out as above; real data run the same loops with
+ * imaginary parts 0, which changes no rounding (every term with an
+ * imaginary factor is an exact zero).
+ */
+
+/* Entry (i, k) of T, as (re, im). */
+static void tget_d(int side, int trans, int cplx, const double *A, int64_t lda,
+                   int64_t i, int64_t k, double *re, double *im)
+{
+    int64_t r = i, c = k;          /* entry (r, c) of op(A) */
+    int64_t ar, ac;                /* entry (ar, ac) of A   */
+    if (side == 1) { r = k; c = i; }
+    if (trans == 0) { ar = r; ac = c; } else { ar = c; ac = r; }
+    if (cplx) {
+        *re = A[2 * (ar + ac * lda)];
+        *im = A[2 * (ar + ac * lda) + 1];
+        if (trans == 2) *im = -*im;
+    } else {
+        *re = A[ar + ac * lda];
+        *im = 0.0;
+    }
+}
+
+int oracle_trsm_d(int side, int uplo, int trans, int diag, int cplx, int64_t m,
+                  int64_t n, double alpha_re, double alpha_im, const double *A,
+                  int64_t lda, double *B, int64_t ldb)
+{
+    int64_t k = side == 0 ? m : n;       /* order of A and of T            */
+    int64_t nrhs = side == 0 ? n : m;    /* number of right-hand sides     */
+    int64_t cs = side == 0 ? 1 : ldb;    /* stride inside one right-hand side */
+    int64_t rs = side == 0 ? ldb : 1;    /* stride between right-hand sides   */
+    int e = cplx ? 2 : 1;
+    int op_lower = (uplo == 0) == (trans == 0);
+    int lower = side == 0 ? op_lower : !op_lower;
+    int64_t q;
+    if (side < 0 || side > 1 || uplo < 0 || uplo > 1 || trans < 0 || trans > 2 ||
+        diag < 0 || diag > 1 || m < 0 || n < 0 || lda < (k > 1 ? k : 1) ||
+        ldb < (m > 1 ? m : 1))
+        return 1;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (q = 0; q < nrhs; ++q) {
+        double *c = B + e * q * rs;
+        int64_t t, u;
+        if (alpha_re == 0.0 && alpha_im == 0.0) {
+            for (t = 0; t < k; ++t) {
+                c[e * t * cs] = 0.0;
+                if (cplx) c[e * t * cs + 1] = 0.0;
+            }
+            continue;
+        }
+        for (t = 0; t < k; ++t) {
+            int64_t i = lower ? t : k - 1 - t;
+            double cr = c[e * i * cs], ci = cplx ? c[e * i * cs + 1] : 0.0;
+            double sr = alpha_re * cr - alpha_im * ci;
+            double si = alpha_re * ci + alpha_im * cr;
+            for (u = 0; u < t; ++u) {
+                int64_t j = lower ? u : k - 1 - u;
+                double tr, ti;
+                double yr = c[e * j * cs], yi = cplx ? c[e * j * cs + 1] : 0.0;
+                tget_d(side, trans, cplx, A, lda, i, j, &tr, &ti);
+                sr = sr - (tr * yr - ti * yi);
+                si = si - (tr * yi + ti * yr);
+            }
+            if (!diag) {
+                double dr, di;
+                tget_d(side, trans, cplx, A, lda, i, i, &dr, &di);
+                if (di == 0.0) {
+                    sr = sr / dr;
+                    si = si / dr;
+                } else {
+                    double den = dr * dr + di * di;
+                    double xr = (sr * dr + si * di) / den;
+                    double xi = (si * dr - sr * di) / den;
+                    sr = xr;
+                    si = xi;
+                }
+            }
+            c[e * i * cs] = sr;
+            if (cplx) c[e * i * cs + 1] = si;
+        }
+    }
+    return 0;
+}
+
+/* The same in fp32 (the operand precision of fp32 and complex fp32). */
+
+static void tget_s(int side, int trans, int cplx, const float *A, int64_t lda,
+                   int64_t i, int64_t k, float *re, float *im)
+{
+    int64_t r = i, c = k;          /* entry (r, c) of op(A) */
+    int64_t ar, ac;                /* entry (ar, ac) of A   */
+    if (side == 1) { r = k; c = i; }
+    if (trans == 0) { ar = r; ac = c; } else { ar = c; ac = r; }
+    if (cplx) {
+        *re = A[2 * (ar + ac * lda)];
+        *im = A[2 * (ar + ac * lda) + 1];
+        if (trans == 2) *im = -*im;
+    } else {
+        *re = A[ar + ac * lda];
+        *im = 0.0f;
+    }
+}
+
+int oracle_trsm_s(int side, int uplo, int trans, int diag, int cplx, int64_t m,
+                  int64_t n, float alpha_re, float alpha_im, const float *A,
+                  int64_t lda, float *B, int64_t ldb)
+{
+    int64_t k = side == 0 ? m : n;       /* order of A and of T            */
+    int64_t nrhs = side == 0 ? n : m;    /* number of right-hand sides     */
+    int64_t cs = side == 0 ? 1 : ldb;    /* stride inside one right-hand side */
+    int64_t rs = side == 0 ? ldb : 1;    /* stride between right-hand sides   */
+    int e = cplx ? 2 : 1;
+    int op_lower = (uplo == 0) == (trans == 0);
+    int lower = side == 0 ? op_lower : !op_lower;
+    int64_t q;
+    if (side < 0 || side > 1 || uplo < 0 || uplo > 1 || trans < 0 || trans > 2 ||
+        diag < 0 || diag > 1 || m < 0 || n < 0 || lda < (k > 1 ? k : 1) ||
+        ldb < (m > 1 ? m : 1))
+        return 1;
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (q = 0; q < nrhs; ++q) {
+        float *c = B + e * q * rs;
+        int64_t t, u;
+        if (alpha_re == 0.0f && alpha_im == 0.0f) {
+            for (t = 0; t < k; ++t) {
+                c[e * t * cs] = 0.0f;
+                if (cplx) c[e * t * cs + 1] = 0.0f;
+            }
+            continue;
+        }
+        for (t = 0; t < k; ++t) {
+            int64_t i = lower ? t : k - 1 - t;
+            float cr = c[e * i * cs], ci = cplx ? c[e * i * cs + 1] : 0.0f;
+            float sr = alpha_re * cr - alpha_im * ci;
+            float si = alpha_re * ci + alpha_im * cr;
+            for (u = 0; u < t; ++u) {
+                int64_t j = lower ? u : k - 1 - u;
+                float tr, ti;
+                float yr = c[e * j * cs], yi = cplx ? c[e * j * cs + 1] : 0.0f;
+                tget_s(side, trans, cplx, A, lda, i, j, &tr, &ti);
+                sr = sr - (tr * yr - ti * yi);
+                si = si - (tr * yi + ti * yr);
+            }
+            if (!diag) {
+                float dr, di;
+                tget_s(side, trans, cplx, A, lda, i, i, &dr, &di);
+                if (di == 0.0f) {
+                    sr = sr / dr;
+                    si = si / dr;
+                } else {
+                    float den = dr * dr + di * di;
+                    float xr = (sr * dr + si * di) / den;
+                    float xi = (si * dr - sr * di) / den;
+                    sr = xr;
+                    si = xi;
+                }
+            }
+            c[e * i * cs] = sr;
+            if (cplx) c[e * i * cs + 1] = si;
+        }
+    }
+    return 0;
+}
+
 /* Number of OpenMP threads a parallel region here would use. */
 int oracle_num_threads(void)
 {

@@ -244,8 +244,47 @@ def check_batched_matches_single(orc, dtype):
         assert bits_equal(np.asfortranarray(Xb[p]), orc.solve(L[p], B[p], a)), (dtype, p)
 
 
+VARIANTS = [(s, u, t, d) for s in "LR" for u in "LU" for t in "NTC" for d in "NU"]
+
+
+def _variant_problem(dtype, side, uplo, diag, m, n, seed):
+    """A with the unused triangle (and, for a unit diagonal, the diagonal)
+    set to NaN: the solve must not read them."""
+    rng = np.random.default_rng(seed)
+    k = m if side == "L" else n
+    A = rng.uniform(-1, 1, (k, k)) / k + np.diag(rng.uniform(1, 2, k))
+    if dtype in CPLX:
+        A = A + 1j * rng.uniform(-1, 1, (k, k)) / k
+    B = rng.uniform(-1, 1, (m, n)) + (1j * rng.uniform(-1, 1, (m, n)) if dtype in CPLX else 0)
+    clean = np.asfortranarray(A.astype(NP[dtype]))
+    poisoned = clean.copy()
+    bad = np.triu(np.ones((k, k), bool), 1) if uplo == "L" else np.tril(np.ones((k, k), bool), -1)
+    if diag == "U":
+        bad |= np.eye(k, dtype=bool)
+    poisoned[bad] = np.nan
+    return clean, np.asfortranarray(poisoned), np.asfortranarray(B.astype(NP[dtype]))
+
+
+def check_variants_scipy(orc, dtype):
+    """Every (side, uplo, trans, diag) against scipy's BLAS ?trsm (for real
+    data trans 'C' is 'T'), with the entries that must not be read set to NaN
+    in the oracle's input."""
+    tol = {"f32": 5e-6, "f64": 1e-14, "c64": 1e-14, "c32": 5e-6}[dtype]
+    trsm = {"f32": sblas.strsm, "f64": sblas.dtrsm, "c64": sblas.ztrsm, "c32": sblas.ctrsm}[dtype]
+    a = 0.75 - 0.25j if dtype in CPLX else -0.75
+    for idx, (side, uplo, trans, diag) in enumerate(VARIANTS):
+        m, n = (13, 7) if idx % 2 else (6, 11)
+        clean, poisoned, B = _variant_problem(dtype, side, uplo, diag, m, n, seed=idx)
+        X = orc.trsm(side, uplo, trans, diag, poisoned, B, a)
+        t = {"N": 0, "T": 1, "C": 2 if dtype in CPLX else 1}[trans]
+        ref = trsm(a, np.array(clean, order="F"), np.array(B, order="F"), side=int(side == "R"),
+                   lower=int(uplo == "L"), trans_a=t, diag=int(diag == "U"))
+        assert np.all(np.isfinite(X)), (dtype, side, uplo, trans, diag)
+        assert nrel(X, ref) < tol, (dtype, side, uplo, trans, diag, nrel(X, ref))
+
+
 QUICK_CHECKS = [check_identity, check_diagonal, check_bidiagonal, check_exact_dyadic,
-                check_scipy, check_batched_matches_single]
+                check_scipy, check_batched_matches_single, check_variants_scipy]
 
 
 # ---------------------------------------------------------------------------
@@ -292,6 +331,17 @@ def test_loop_order_invariance(orc):
             for j in sorted({0, n // 2, n - 1}):
                 xj = orc.solve(L, np.asfortranarray(B[:, j:j + 1]), a)
                 assert bits_equal(xj[:, 0], Xc[:, j])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_variant_oracle_left_lower_is_the_pinned_solve(orc, dtype):
+    """The general oracle at (side L, lower, no transpose, non-unit) runs the
+    same operations in the same order as the pinned left-lower solve:
+    bitwise equal."""
+    for m, n in [(1, 1), (64, 64), (150, 37)]:
+        L, B = make_problem(dtype, m, n, seed=m + 2 * n)
+        a = 0.5 - 0.25j if dtype in CPLX else 0.5
+        assert bits_equal(orc.trsm("L", "L", "N", "N", L, B, a), orc.solve(L, B, a)), (dtype, m, n)
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -402,6 +452,13 @@ MUTANTS = [
      "b[2 * i + 1] = ar * bi;"),
     ("c_batched_stride", "oracle_lln_c_batched", "solve_column_c(m, alpha_re, alpha_im, A + 2 * p * strideA, lda,",
      "solve_column_c(m, alpha_re, alpha_im, A + p * strideA, lda,"),
+    ("trsm_right_untransposed", "tget_d", "if (side == 1) { r = k; c = i; }", "if (side == 1) { r = i; c = k; }"),
+    ("trsm_no_conj", "tget_d", "if (trans == 2) *im = -*im;", "if (trans == 3) *im = -*im;"),
+    ("trsm_wrong_triangle", "oracle_trsm_d", "int op_lower = (uplo == 0) == (trans == 0);",
+     "int op_lower = (uplo == 0);"),
+    ("trsm_unit_divides", "oracle_trsm_d", "if (!diag) {", "if (1) {"),
+    ("trsm_s_alpha_im_sign", "oracle_trsm_s", "float si = alpha_re * ci + alpha_im * cr;",
+     "float si = alpha_re * ci - alpha_im * cr;"),
     ("batched_stride", "oracle_lln_d_batched", "solve_column_d(m, alpha, A + p * strideA, lda,",
      "solve_column_d(m, alpha, A, lda,"),
 ]
