@@ -108,6 +108,35 @@ trsm_status_t trsm_lln_ex(trsm_dtype_t dtype, int64_t m, int64_t n, const void *
                           const void *A, int64_t lda, void *B, int64_t ldb, int ib,
                           int force_blocked, hipStream_t stream);
 
+/* ---- the general TRSM: every side, triangle, transposition, diagonal ---- */
+
+typedef enum trsm_side_t { TRSM_LEFT = 0, TRSM_RIGHT = 1 } trsm_side_t;
+typedef enum trsm_fill_t { TRSM_LOWER = 0, TRSM_UPPER = 1 } trsm_fill_t;
+typedef enum trsm_op_t { TRSM_OP_N = 0, TRSM_OP_T = 1, TRSM_OP_C = 2 } trsm_op_t;
+typedef enum trsm_diag_t { TRSM_NON_UNIT = 0, TRSM_UNIT = 1 } trsm_diag_t;
+
+/*
+ * BLAS TRSM (the pages' system op(A) X = alpha B of section 2.1, and its
+ * right-side form):
+ *   side TRSM_LEFT:  op(A) X = alpha B, A is m x m (lda >= max(1, m));
+ *   side TRSM_RIGHT: X op(A) = alpha B, A is n x n (lda >= max(1, n));
+ *   uplo: the triangle of A that is used (the other is never read);
+ *   trans: op(A) = A, A^T or A^H (TRSM_OP_C; for real types the same as T);
+ *   diag TRSM_UNIT: unit diagonal, the diagonal of A is never read.
+ *   B: m x n, ldb >= max(1, m), overwritten with X.  Other arguments and the
+ *   quick returns as for trsm_lln.
+ * trsm_solve(LEFT, LOWER, OP_N, NON_UNIT, ...) is trsm_lln.  Every other case is brought to
+ * it by index reflection: the triangle of op(A) (or op(A)^T for the right
+ * side) is copied, transposed, conjugated or reversed as needed, into a
+ * library workspace (order^2 elements) and solved there; when the
+ * right-hand sides need reordering too, B is staged there as well (m*n
+ * elements more) and copied back.  The staging workspace is cached per
+ * (device, stream) beside the solve's and freed by trsm_release_workspace.
+ */
+trsm_status_t trsm_solve(trsm_side_t side, trsm_fill_t uplo, trsm_op_t trans, trsm_diag_t diag,
+                         trsm_dtype_t dtype, int64_t m, int64_t n, const void *alpha,
+                         const void *A, int64_t lda, void *B, int64_t ldb, hipStream_t stream);
+
 /*
  * Block size the blocked path uses for (dtype, m, n): nearest-scale match
  * in the table built by offline profiling on MI355X (section 4.3.2).

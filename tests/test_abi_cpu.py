@@ -142,3 +142,25 @@ def test_profiler_bookkeeping_without_launches(T):
     T.trsm_profile_stop()
     with pytest.raises(T.TrsmError):
         T.trsm_profile_read(0)
+
+
+@pytest.mark.parametrize("flags,dims", [
+    ((2, 0, 0, 0), (4, 3, 4, 4)), ((0, 2, 0, 0), (4, 3, 4, 4)), ((0, 0, 3, 0), (4, 3, 4, 4)),
+    ((0, 0, 0, 2), (4, 3, 4, 4)), ((-1, 0, 0, 0), (4, 3, 4, 4)),
+    ((1, 0, 0, 0), (4, 6, 5, 4)),   # right side: A is n x n, lda < n
+    ((0, 1, 1, 1), (4, 3, 3, 4)),   # left side: lda < m
+    ((1, 1, 2, 0), (4, 3, 3, 3)),   # ldb < m
+])
+def test_general_solve_rejects_bad_arguments(T, flags, dims):
+    m, n, lda, ldb = dims
+    al = T.alpha_buffer(1, 1.0)
+    assert T.lib.trsm_solve(*flags, 1, m, n, ctypes.addressof(al), FAKE, lda, FAKE, ldb, None) == 1
+
+
+def test_general_solve_quick_returns(T):
+    al = T.alpha_buffer(1, 1.0)
+    a = ctypes.addressof(al)
+    for side in (0, 1):
+        assert T.lib.trsm_solve(side, 1, 2, 1, 1, 0, 5, a, None, 5, None, 1, None) == 0   # m == 0
+        assert T.lib.trsm_solve(side, 1, 2, 1, 1, 5, 0, a, None, 5, None, 5, None) == 0   # n == 0
+    assert T.lib.trsm_solve(0, 0, 0, 0, 9, 4, 3, a, FAKE, 4, FAKE, 4, None) == 1         # dtype

@@ -4,6 +4,7 @@ Argument marshalling only: every step of the solve runs in the library's HIP
 kernels.  The functions carry the names of the C ABI (include/trsm.h):
 
     trsm_lln(A, B, alpha=1.0, *, stream=None)                      -> B
+    trsm_solve(A, B, alpha=1.0, *, side, uplo, trans, diag, stream=None) -> B
     trsm_lln_strided_batched(A, B, alpha=1.0, *, stream=None)      -> B
     trsm_lln_ex(A, B, alpha=1.0, ib=0, force_blocked=False, *, stream=None) -> B
     trsm_lln_select_ib(dtype, m, n)                                -> int
@@ -14,8 +15,9 @@ A and B are torch tensors on the GPU in column-major storage: for an m x n
 operand, stride(0) == 1 and stride(1) == ld >= m (``colmajor_empty`` makes
 one).  Batched operands are (batch, m, n) with strides (stride, 1, ld).
 Supported dtypes: torch.float32, torch.float64, torch.complex64,
-torch.complex128.  B is
-overwritten with X such that L X = alpha B, L the lower triangle of A.
+torch.complex128.  B is overwritten with X such that L X = alpha B, L the
+lower triangle of A (trsm_solve: the general op(A) X = alpha B or
+X op(A) = alpha B).
 
 The library must have been built (``python triangular_solve_trsm_amd/build.py``
 or ``__graft_entry__.build()``); importing this package without it raises.
@@ -33,7 +35,7 @@ STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "ALLOC_FAILED", 3: "HIP_ERROR", 4
 IB_CHOICES = (64, 128, 256, 512, 1024)
 
 # Every symbol include/trsm.h and include/trsm_kernels.h declare.
-EXPORTS = ("trsm_lln", "trsm_lln_strided_batched", "trsm_lln_ex", "trsm_lln_select_ib",
+EXPORTS = ("trsm_lln", "trsm_solve", "trsm_lln_strided_batched", "trsm_lln_ex", "trsm_lln_select_ib",
            "trsm_status_string", "trsm_release_workspace",
            "trsm_kernel_diag_inv", "trsm_kernel_gemm",
            "trsm_profile_start", "trsm_profile_stop", "trsm_profile_count", "trsm_profile_read")
@@ -65,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.trsm_lln_strided_batched.argtypes = [ci, i64, i64, vp, vp, i64, i64, vp, i64, i64, i64, vp]
     lib.trsm_lln_strided_batched.restype = ci
     lib.trsm_lln_ex.argtypes = [ci, i64, i64, vp, vp, i64, vp, i64, ci, ci, vp]
+    lib.trsm_solve.argtypes = [ci, ci, ci, ci, ci, i64, i64, vp, vp, i64, vp, i64, vp]
+    lib.trsm_solve.restype = ci
     lib.trsm_lln_ex.restype = ci
     lib.trsm_lln_select_ib.argtypes = [ci, i64, i64]
     lib.trsm_lln_select_ib.restype = ci
@@ -160,6 +164,27 @@ def trsm_lln(A, B, alpha=1.0, *, stream=None):
     st = lib.trsm_lln(code, m, n, ctypes.addressof(al), A.data_ptr(), _ld(A, m, m),
                       B.data_ptr(), _ld(B, m, n), _stream_handle(stream))
     _check(st, "trsm_lln")
+    return B
+
+
+def trsm_solve(A, B, alpha=1.0, *, side="L", uplo="L", trans="N", diag="N", stream=None):
+    """General TRSM in place (B <- X): op(A) X = alpha B for side 'L' (A is
+    m x m), X op(A) = alpha B for side 'R' (A is n x n); uplo 'L' / 'U' is the
+    triangle of A used, trans 'N' / 'T' / 'C' gives op(A) = A, A^T, A^H, and
+    diag 'U' means a unit diagonal that is not read."""
+    code = _dtype_code(B)
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    m, n = B.shape
+    k = m if side == "L" else n
+    if tuple(A.shape) != (k, k):
+        raise ValueError(f"A must be {k} x {k}")
+    flags = ({"L": 0, "R": 1}[side], {"L": 0, "U": 1}[uplo], {"N": 0, "T": 1, "C": 2}[trans],
+             {"N": 0, "U": 1}[diag])
+    al = alpha_buffer(code, alpha)
+    st = lib.trsm_solve(*flags, code, m, n, ctypes.addressof(al), A.data_ptr(), _ld(A, k, k),
+                        B.data_ptr(), _ld(B, m, n), _stream_handle(stream))
+    _check(st, "trsm_solve")
     return B
 
 

@@ -26,6 +26,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "trsm.h"
@@ -61,7 +62,10 @@ struct DevInfo {
     int cus;   // compute units
 };
 std::map<int, DevInfo> g_dev;                                  // device -> properties
-std::map<std::pair<int, hipStream_t>, std::pair<void *, size_t>> g_ws;
+// Workspace per (device, stream, slot): slot 0 serves the solve (inverses,
+// panel), slot 1 the staging copies of the general variants, which stay in
+// use while the solve runs.
+std::map<std::tuple<int, hipStream_t, int>, std::pair<void *, size_t>> g_ws;
 
 trsm_status_t check_device(int *dev_out, int *cus_out = nullptr) {
     int dev = 0;
@@ -79,9 +83,9 @@ trsm_status_t check_device(int *dev_out, int *cus_out = nullptr) {
     return it->second.ok ? TRSM_STATUS_SUCCESS : TRSM_STATUS_NOT_SUPPORTED;
 }
 
-trsm_status_t get_workspace(int dev, hipStream_t st, size_t bytes, void **out) {
+trsm_status_t get_workspace(int dev, hipStream_t st, size_t bytes, void **out, int slot = 0) {
     std::lock_guard<std::mutex> lk(g_mu);
-    auto &e = g_ws[{dev, st}];
+    auto &e = g_ws[std::make_tuple(dev, st, slot)];
     if (e.second < bytes) {
         if (e.first) {
             if (hipStreamSynchronize(st) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
@@ -410,6 +414,78 @@ trsm_status_t trsm_lln_strided_batched(trsm_dtype_t dtype, int64_t m, int64_t n,
     }
 }
 
+trsm_status_t trsm_solve(trsm_side_t side, trsm_fill_t uplo, trsm_op_t trans, trsm_diag_t diag,
+                         trsm_dtype_t dtype, int64_t m, int64_t n, const void *alpha,
+                         const void *A, int64_t lda, void *B, int64_t ldb, hipStream_t stream) {
+    try {
+        if ((side != TRSM_LEFT && side != TRSM_RIGHT) || (uplo != TRSM_LOWER && uplo != TRSM_UPPER) ||
+            (trans != TRSM_OP_N && trans != TRSM_OP_T && trans != TRSM_OP_C) ||
+            (diag != TRSM_NON_UNIT && diag != TRSM_UNIT) || !valid_dtype(dtype) || m < 0 || n < 0)
+            return TRSM_STATUS_INVALID_VALUE;
+        const int64_t k = side == TRSM_LEFT ? m : n;  // order of A
+        if (lda < (k > 1 ? k : 1) || ldb < (m > 1 ? m : 1)) return TRSM_STATUS_INVALID_VALUE;
+        if (m > 0 && n > 0 && (A == nullptr || B == nullptr || alpha == nullptr))
+            return TRSM_STATUS_INVALID_VALUE;
+        if (m > 0 && n > 0 && (ldb > INT64_MAX / n || lda > INT64_MAX / k)) return TRSM_STATUS_INVALID_VALUE;
+        if (m == 0 || n == 0) return TRSM_STATUS_SUCCESS;
+        if (side == TRSM_LEFT && uplo == TRSM_LOWER && trans == TRSM_OP_N && diag == TRSM_NON_UNIT)
+            return run(dtype, m, n, alpha, A, lda, 0, B, ldb, 0, 1, 0, false, stream);
+        int dev = 0;
+        trsm_status_t s = check_device(&dev);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        const Scalar al = read_alpha(dtype, alpha);
+        if (al.re == 0.0 && al.im == 0.0) {
+            LaunchTimer t(TRSM_KERNEL_FILL, dtype, m, n, 0, 1, stream);
+            return hip_status(fill_zero_launch(dtype, m, n, B, ldb, 0, 1, stream));
+        }
+        // Every variant is a left-lower solve E' X' = alpha B' (section 2.1's
+        // system).  E = op(A) on the left; on the right X op(A) = alpha B is
+        // op(A)^T X^T = alpha B^T, so E = op(A)^T and the right-hand sides are
+        // the rows of B.  An upper E becomes lower by reversing the order of
+        // the unknowns: E' = J E J, B' = J B (J the reversal permutation).
+        const bool e_trans = side == TRSM_LEFT ? trans != TRSM_OP_N : trans == TRSM_OP_N;
+        const bool op_lower = (uplo == TRSM_LOWER) == (trans == TRSM_OP_N);
+        const bool e_lower = side == TRSM_LEFT ? op_lower : !op_lower;
+        const int rev = e_lower ? 0 : 1;
+        const int64_t nrhs = side == TRSM_LEFT ? n : m;
+        const bool b_in_place = side == TRSM_LEFT && !rev;  // B is already B'
+        const size_t es = dtype_size(dtype);
+        const size_t abytes = ((size_t)k * (size_t)k * es + 255) & ~(size_t)255;
+        const size_t bbytes = b_in_place ? 0 : (size_t)k * (size_t)nrhs * es;
+        void *ws = nullptr;
+        s = get_workspace(dev, stream, abytes + bbytes, &ws, 1);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        void *Ap = ws;
+        void *Bp = static_cast<char *>(ws) + abytes;
+        if (log_enabled())
+            std::fprintf(stderr, "[trsm] variant side=%d uplo=%d trans=%d diag=%d: E %s%s\n", side,
+                         uplo, trans, diag, e_trans ? "transposed" : "direct", rev ? ", reversed" : "");
+        const Reflect fa{rev, rev, e_trans ? 1 : 0, trans == TRSM_OP_C ? 1 : 0, 1,
+                         diag == TRSM_UNIT ? 1 : 0};
+        {
+            LaunchTimer t(TRSM_KERNEL_COPY, dtype, k, k, 0, 1, stream);
+            if (transform_launch(dtype, k, k, A, lda, Ap, k, fa, stream) != hipSuccess)
+                return TRSM_STATUS_HIP_ERROR;
+        }
+        if (b_in_place) return run(dtype, k, nrhs, alpha, Ap, k, 0, B, ldb, 0, 1, 0, false, stream);
+        // B'(i, j) = B(rev ? k-1-i : i, j) on the left, B(j, rev ? k-1-i : i) on the right
+        const Reflect fb{rev, 0, side == TRSM_RIGHT ? 1 : 0, 0, 0, 0};
+        {
+            LaunchTimer t(TRSM_KERNEL_COPY, dtype, k, nrhs, 0, 1, stream);
+            if (transform_launch(dtype, k, nrhs, B, ldb, Bp, k, fb, stream) != hipSuccess)
+                return TRSM_STATUS_HIP_ERROR;
+        }
+        s = run(dtype, k, nrhs, alpha, Ap, k, 0, Bp, k, 0, 1, 0, false, stream);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        // back: B(i, j) = B'(rev ? m-1-i : i, j) on the left, B'(rev ? n-1-j : j, i) on the right
+        const Reflect fx = side == TRSM_LEFT ? Reflect{rev, 0, 0, 0, 0, 0} : Reflect{0, rev, 1, 0, 0, 0};
+        LaunchTimer t(TRSM_KERNEL_COPY, dtype, m, n, 0, 1, stream);
+        return hip_status(transform_launch(dtype, m, n, Bp, k, B, ldb, fx, stream));
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
 trsm_status_t trsm_lln_ex(trsm_dtype_t dtype, int64_t m, int64_t n, const void *alpha,
                           const void *A, int64_t lda, void *B, int64_t ldb, int ib,
                           int force_blocked, hipStream_t stream) {
@@ -566,7 +642,7 @@ trsm_status_t trsm_release_workspace(void) {
         const bool have_cur = hipGetDevice(&cur) == hipSuccess;
         for (auto &kv : g_ws) {
             if (!kv.second.first) continue;
-            if (hipSetDevice(kv.first.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+            if (hipSetDevice(std::get<0>(kv.first)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
                 s = TRSM_STATUS_HIP_ERROR;
             (void)hipFree(kv.second.first);
         }

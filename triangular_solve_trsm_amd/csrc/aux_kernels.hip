@@ -1,6 +1,7 @@
 // Small memory kernels around the solve: zeroing B (alpha == 0, where the
-// result is X = 0 and A is not read) and copying one panel of B into the
-// panel buffer that the first diagonal-block solve reads.
+// result is X = 0 and A is not read), copying one panel of B into the
+// panel buffer that the first diagonal-block solve reads, and the index
+// reflections that bring the other TRSM variants to the left-lower form.
 #include "scalar_ops.h"
 
 namespace trsm {
@@ -34,6 +35,57 @@ __global__ __launch_bounds__(256) void copy_panel_kernel(int64_t rows, int64_t n
     }
 }
 
+// dst(i, j) = f(src(a, b)) for an R x C dst, with a = revR ? R-1-i : i and
+// b = revC ? C-1-j : j; src(a, b) is src[a + b*lds], or src[b + a*lds] when
+// trans (src then holds the transposed matrix); f conjugates when conj.
+// lower: only i >= j is written (and read); unit: dst(i, i) = 1 without
+// reading src.  32 x 32 tiles of dst per workgroup; the transposing form
+// goes through LDS so that both the reads and the writes are coalesced.
+template <typename T>
+__device__ __forceinline__ T conj_if(T v, int) { return v; }
+template <>
+__device__ __forceinline__ cplx conj_if<cplx>(cplx v, int c) { return c ? cplx{v.re, -v.im} : v; }
+template <>
+__device__ __forceinline__ cplx32 conj_if<cplx32>(cplx32 v, int c) { return c ? cplx32{v.re, -v.im} : v; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void transform_kernel(int64_t R, int64_t C,
+                                                        const T *__restrict__ src, int64_t lds,
+                                                        T *__restrict__ dst, int64_t ldd, int revR,
+                                                        int revC, int trans, int conj, int lower,
+                                                        int unit) {
+    __shared__ T tile[32][33];
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+    const int64_t i0 = (int64_t)blockIdx.x * 32, j0 = (int64_t)blockIdx.y * 32;
+    if (lower && i0 + 31 < j0) return;  // tile wholly above the diagonal (uniform)
+    auto wanted = [&](int64_t i, int64_t j) { return i < R && j < C && (!lower || i >= j); };
+    auto put = [&](int64_t i, int64_t j, T v) {
+        dst[i + j * ldd] = (unit && i == j) ? Elem<T>::one() : conj_if<T>(v, conj);
+    };
+    if (!trans) {
+        for (int jj = ty; jj < 32; jj += 8) {
+            const int64_t i = i0 + tx, j = j0 + jj;
+            if (!wanted(i, j)) continue;
+            const int64_t a = revR ? R - 1 - i : i, b = revC ? C - 1 - j : j;
+            put(i, j, (unit && i == j) ? Elem<T>::one() : src[a + b * lds]);
+        }
+        return;
+    }
+    // read src(b, a) with consecutive threads on consecutive b (src rows)
+    for (int ii = ty; ii < 32; ii += 8) {
+        const int64_t i = i0 + ii, j = j0 + tx;
+        if (wanted(i, j) && !(unit && i == j)) {
+            const int64_t a = revR ? R - 1 - i : i, b = revC ? C - 1 - j : j;
+            tile[ii][tx] = src[b + a * lds];
+        }
+    }
+    __syncthreads();
+    for (int jj = ty; jj < 32; jj += 8) {
+        const int64_t i = i0 + tx, j = j0 + jj;
+        if (wanted(i, j)) put(i, j, tile[tx][jj]);
+    }
+}
+
 inline unsigned grid_for(int64_t total) {
     int64_t g = (total + 255) / 256;
     if (g > 65536) g = 65536;  // grid-stride loops cover the rest
@@ -60,7 +112,30 @@ hipError_t copy_t(int64_t rows, int64_t n, const void *src, int64_t lds, void *d
     return hipGetLastError();
 }
 
+template <typename T>
+hipError_t transform_t(int64_t R, int64_t C, const void *src, int64_t lds, void *dst, int64_t ldd,
+                       const Reflect &f, hipStream_t st) {
+    if (R <= 0 || C <= 0) return hipSuccess;
+    const int64_t gx = (R + 31) / 32, gy = (C + 31) / 32;
+    if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((transform_kernel<T>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st, R,
+                       C, static_cast<const T *>(src), lds, static_cast<T *>(dst), ldd, f.revR,
+                       f.revC, f.trans, f.conj, f.lower, f.unit);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t transform_launch(int dtype, int64_t R, int64_t C, const void *src, int64_t lds,
+                            void *dst, int64_t ldd, const Reflect &f, hipStream_t stream) {
+    switch (dtype) {
+        case R32F: return transform_t<float>(R, C, src, lds, dst, ldd, f, stream);
+        case R64F: return transform_t<double>(R, C, src, lds, dst, ldd, f, stream);
+        case C64F: return transform_t<cplx>(R, C, src, lds, dst, ldd, f, stream);
+        case C32F: return transform_t<cplx32>(R, C, src, lds, dst, ldd, f, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t fill_zero_launch(int dtype, int64_t m, int64_t n, void *B, int64_t ldb,
                             int64_t strideB, int64_t batch, hipStream_t stream) {

@@ -89,5 +89,15 @@ hipError_t fill_zero_launch(int dtype, int64_t m, int64_t n, void *B, int64_t ld
 // dst (rows x n, ldd) <- src (rows x n, lds).
 hipError_t copy_panel_launch(int dtype, int64_t rows, int64_t n, const void *src,
                              int64_t lds, void *dst, int64_t ldd, hipStream_t stream);
+// Index reflection of an R x C dst from src:
+//   dst(i, j) = f(src(a, b)),  a = revR ? R-1-i : i,  b = revC ? C-1-j : j,
+// src(a, b) at src[a + b*lds], or at src[b + a*lds] when trans; f conjugates
+// when conj (complex types).  lower: only i >= j is read and written.
+// unit: dst(i, i) = 1 (src's diagonal is not read).
+struct Reflect {
+    int revR, revC, trans, conj, lower, unit;
+};
+hipError_t transform_launch(int dtype, int64_t R, int64_t C, const void *src, int64_t lds,
+                            void *dst, int64_t ldd, const Reflect &f, hipStream_t stream);
 
 }  // namespace trsm
