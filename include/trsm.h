@@ -139,7 +139,9 @@ trsm_status_t trsm_solve(trsm_side_t side, trsm_fill_t uplo, trsm_op_t trans, tr
 
 /*
  * Block size the blocked path uses for (dtype, m, n): nearest-scale match
- * in the table built by offline profiling on MI355X (section 4.3.2).
+ * in the table built by offline profiling on MI355X (section 4.3.2), the
+ * scale being (m, n) compared in log space (the table holds square
+ * problems and narrow ones, n = 64, 256, 1024).
  * Returns 0 for an invalid dtype or negative size.  Pure, thread-safe.
  */
 int trsm_lln_select_ib(trsm_dtype_t dtype, int64_t m, int64_t n);

@@ -40,7 +40,7 @@ namespace {
 
 struct IbEntry {
     int dtype;
-    int64_t m;
+    int64_t m, n;  // the profiled problem: order of L, right-hand-side columns
     int ib;
     int left;  // phase-2 schedule that measured faster: 1 left-looking, 0 right-looking
 };
@@ -195,13 +195,17 @@ constexpr int64_t kLeftMinTiles = 1024;
 
 bool valid_ib(int ib) { return ib == 64 || ib == 128 || ib == 256 || ib == 512 || ib == 1024; }
 
-// Nearest tabulated order for this data type (section 4.3.2: online lookup).
-IbEntry select_entry(int dt, int64_t m) {
-    IbEntry best{dt, 0, 256, 0};
-    int64_t bestd = INT64_MAX;
+// Nearest tabulated problem for this data type (section 4.3.2: online
+// lookup, nearest match).  The table is profiled at several (m, n); scale
+// is compared in log space, |log2(m/m_e)| + |log2(n/n_e)|, so that a narrow
+// B finds the narrow entries and a square one the square entries.
+IbEntry select_entry(int dt, int64_t m, int64_t n) {
+    IbEntry best{dt, 0, 0, 256, 0};
+    double bestd = 1e300;
+    const double lm = std::log2((double)(m > 1 ? m : 1)), ln = std::log2((double)(n > 1 ? n : 1));
     for (const IbEntry &e : kIbTable) {
         if (e.dtype != dt) continue;
-        const int64_t d = e.m > m ? e.m - m : m - e.m;
+        const double d = std::fabs(std::log2((double)e.m) - lm) + std::fabs(std::log2((double)e.n) - ln);
         if (d < bestd) {
             bestd = d;
             best = e;
@@ -210,7 +214,7 @@ IbEntry select_entry(int dt, int64_t m) {
     return best;
 }
 
-int select_ib(int dt, int64_t m) { return select_entry(dt, m).ib; }
+int select_ib(int dt, int64_t m, int64_t n) { return select_entry(dt, m, n).ib; }
 
 // Phase 2 schedule.  Left-looking is the pages' order (section 4.3 "Phase 2"):
 // block row r+1 is updated once, by all solved rows, with K = (r+1)*ib.
@@ -370,7 +374,7 @@ trsm_status_t run(int dt, int64_t m, int64_t n, const void *alpha_p, const void 
         LaunchTimer t(TRSM_KERNEL_SMALL, dt, m, n, 0, batch, st);
         return hip_status(small_lln_launch(dt, (int)m, n, alpha, A, lda, sA, B, ldb, sB, batch, st));
     }
-    const IbEntry cfg = select_entry(dt, m);
+    const IbEntry cfg = select_entry(dt, m, n);
     const int ib = ib_forced ? ib_forced : cfg.ib;
     const size_t es = dtype_size(dt);
     for (int64_t p = 0; p < batch; ++p) {
@@ -620,7 +624,7 @@ trsm_status_t trsm_profile_read(int64_t i, trsm_profile_record_t *rec) {
 
 int trsm_lln_select_ib(trsm_dtype_t dtype, int64_t m, int64_t n) {
     if (!valid_dtype(dtype) || m < 0 || n < 0) return 0;
-    return select_ib(dtype, m);
+    return select_ib(dtype, m, n);
 }
 
 const char *trsm_status_string(trsm_status_t status) {
