@@ -164,3 +164,33 @@ def test_general_solve_quick_returns(T):
         assert T.lib.trsm_solve(side, 1, 2, 1, 1, 0, 5, a, None, 5, None, 1, None) == 0   # m == 0
         assert T.lib.trsm_solve(side, 1, 2, 1, 1, 5, 0, a, None, 5, None, 5, None) == 0   # n == 0
     assert T.lib.trsm_solve(0, 0, 0, 0, 9, 4, 3, a, FAKE, 4, FAKE, 4, None) == 1         # dtype
+
+
+def _table():
+    """(dtype code, m, n) -> (ib, left) from the committed block-size table."""
+    import re
+    here = os.path.dirname(os.path.abspath(__file__))
+    src = open(os.path.join(here, "..", "triangular_solve_trsm_amd", "csrc", "ib_table.inc")).read()
+    codes = {"R32F": 0, "R64F": 1, "C64F": 2, "C32F": 3}
+    out = {}
+    for dt, m, n, ib, left in re.findall(r"\{(R32F|R64F|C64F|C32F), (\d+), (\d+), (\d+), ([01])\}", src):
+        out[(codes[dt], int(m), int(n))] = (int(ib), int(left))
+    return out
+
+
+def test_block_size_lookup_matches_table(T):
+    """Online lookup of section 4.3.2: at every profiled (m, n) the library
+    returns that entry's block size; between entries it returns the entry
+    nearest in log distance |log2(m/m_e)| + |log2(n/n_e)|."""
+    import math
+    table = _table()
+    assert len(table) >= 4 * 20, "table should cover four types at many (m, n)"
+    for (dt, m, n), (ib, _) in table.items():
+        assert T.trsm_lln_select_ib(dt, m, n) == ib, (dt, m, n)
+    for dt in range(4):
+        entries = [(m, n, v[0]) for (d, m, n), v in table.items() if d == dt]
+        for m, n in [(100, 100), (3000, 3000), (3000, 100), (6000, 300), (20000, 50), (700, 5000)]:
+            dist = lambda e: abs(math.log2(e[0] / m)) + abs(math.log2(e[1] / n))
+            best = min(dist(e) for e in entries)
+            allowed = {e[2] for e in entries if abs(dist(e) - best) < 1e-9}  # ties: any of them
+            assert T.trsm_lln_select_ib(dt, m, n) in allowed, (dt, m, n)
