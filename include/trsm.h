@@ -30,9 +30,10 @@
  * convention): a zero on the diagonal yields Inf/NaN in X.
  *
  * Workspace: the blocked path (m > 64) needs device scratch space for the
- * inverted diagonal blocks and one panel of B.  The library allocates it per
- * (device, stream), grows it on demand and keeps it until
- * trsm_release_workspace().  Calls on the same stream are ordered and share
+ * inverted diagonal blocks, one panel of B and, when B is narrow, the
+ * partial sums of products split along K (at most 2^21 elements).  The
+ * library allocates it per (device, stream), grows it on demand and keeps
+ * it until trsm_release_workspace().  Calls on the same stream are ordered and share
  * it safely; concurrent calls on different streams each get their own.
  */
 #ifndef TRSM_MI355X_H

@@ -150,6 +150,40 @@ def test_both_phase2_schedules(T, dtype, schedule, ib, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
+@pytest.mark.parametrize("schedule", ["left", "right"])
+@pytest.mark.parametrize("splitk", ["0", "1024", "65536"])
+@pytest.mark.parametrize("n", [1, 37, 64])
+def test_split_k_phase2(T, dtype, schedule, splitk, n, monkeypatch):
+    """Narrow B: solve and update products with few output tiles are cut
+    along K into chunks whose partial sums are reduced afterwards.  Split-K
+    off (0), at the default workgroup target and at a target that splits
+    every product to the smallest chunk; m = 2000 with ib = 512 gives split
+    K = 512 solves, a ragged last block (K = 464) that cannot be split, and
+    left-looking updates with K up to 1536."""
+    monkeypatch.setenv("TRSM_SCHEDULE", schedule)
+    monkeypatch.setenv("TRSM_SPLITK", splitk)
+    m = 2000
+    L, B = make_problem(dtype, m, n, seed=2000 + n)
+    a = 0.75 - 0.5j if dtype in CPLX else 0.75
+    X = solve_gpu(T, L, B, a, ib=512)
+    check(dtype, X, oracle.solve(L, B, a), f"{dtype} {schedule} splitk={splitk} n={n}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
+@pytest.mark.parametrize("schedule", ["left", "right"])
+def test_split_k_bidiagonal_exact(T, dtype, schedule, monkeypatch):
+    """The running-sum problem stays exact when K is split: every partial sum
+    is a small integer, so the reduction of the chunks is exact too."""
+    monkeypatch.setenv("TRSM_SCHEDULE", schedule)
+    monkeypatch.setenv("TRSM_SPLITK", "65536")
+    m = 2048
+    L = unit_bidiagonal_minus_one(m, dtype)
+    B = small_integer_rhs(m, 16, dtype, seed=m)
+    X = solve_gpu(T, L, B, 1.0, ib=512)
+    assert np.array_equal(X, np.cumsum(B, axis=0)), f"{dtype} {schedule}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_m_4097_narrow(T, dtype):
     m, n = 4097, 19
     L, B = make_problem(dtype, m, n, seed=4097)

@@ -20,6 +20,7 @@
 // block row, whose M x N extent keeps all 256 CUs busy early on.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -28,11 +29,11 @@
 #include <mutex>
 #include <tuple>
 #include <utility>
+#include <vector>
 
 #include "trsm.h"
 #include "trsm_internal.h"
 #include "trsm_kernels.h"
-#include <vector>
 
 using namespace trsm;
 
@@ -233,6 +234,23 @@ bool use_left_looking(int dt, int64_t m, int64_t n, int ib, bool table_left) {
     return ((rows + 63) / 64) * ((n + 63) / 64) >= kLeftMinTiles;
 }
 
+// Split-K target for phase 2: a product with so few 64 x 32 tiles that
+// fewer than this many workgroups would run is cut along K (a narrow B gives
+// solve and update products a handful of tiles each with a K of ib or
+// more).  TRSM_SPLITK=<workgroups> overrides it, 0 turns split-K off (tuning
+// and tests).
+constexpr int64_t kSplitKTarget = 1024;
+
+int64_t splitk_target() {
+    const char *e = std::getenv("TRSM_SPLITK");
+    if (e && e[0] != '\0') {
+        char *end = nullptr;
+        const long long v = std::strtoll(e, &end, 10);
+        if (end != e && *end == '\0' && v >= 0) return (int64_t)v;
+    }
+    return kSplitKTarget;
+}
+
 // Blocked path for one problem (m > 0, n > 0, alpha != 0).
 trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void *A,
                           int64_t lda, void *B, int64_t ldb, int ib, bool table_left, int dev,
@@ -247,11 +265,31 @@ trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void
     size_t pbytes = (size_t)ib * n * es;
     const size_t tbytes = (size_t)diag_inv_tmp_elems(ib, m) * es;
     if (tbytes > pbytes) pbytes = tbytes;
+    pbytes = (pbytes + 255) & ~(size_t)255;
+    // split-K factor of every phase-2 product, and the partial sums they need
+    const int64_t target = splitk_target();
+    std::vector<int> solve_parts((size_t)nb, 1), update_parts((size_t)nb, 1);
+    int64_t part_elems = 0;
+    for (int64_t r = 0; r < nb; ++r) {
+        const int64_t r0 = r * ib;
+        const int64_t bs = (m - r0) < ib ? (m - r0) : ib;
+        int p = gemm_splitk_parts(dt, bs, n, bs, target);
+        solve_parts[(size_t)r] = p;
+        if (p > 1) part_elems = std::max(part_elems, p * bs * n);
+        if (r + 1 == nb) break;
+        const int64_t mrest = m - r0 - bs;
+        const int64_t bsn = mrest < ib ? mrest : ib;
+        p = left ? gemm_splitk_parts(dt, bsn, n, r0 + bs, target)
+                 : gemm_splitk_parts(dt, mrest, n, bs, target);
+        update_parts[(size_t)r] = p;
+        if (p > 1) part_elems = std::max(part_elems, p * (left ? bsn : mrest) * n);
+    }
     void *ws = nullptr;
-    trsm_status_t s = get_workspace(dev, st, wbytes + pbytes, &ws);
+    trsm_status_t s = get_workspace(dev, st, wbytes + pbytes + (size_t)part_elems * es, &ws);
     if (s != TRSM_STATUS_SUCCESS) return s;
     char *W = static_cast<char *>(ws);
     void *P = W + wbytes;
+    void *Part = part_elems > 0 ? W + wbytes + pbytes : nullptr;
     const char *Ab = static_cast<const char *>(A);
     char *Bb = static_cast<char *>(B);
     if (log_enabled())
@@ -296,7 +334,7 @@ trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void
         sg.a_lower = 1;
         {
             LaunchTimer t(TRSM_KERNEL_SOLVE_GEMM, dt, bs, n, bs, 1, st);
-            e = gemm_launch(dt, sg, st);
+            e = gemm_splitk_launch(dt, sg, solve_parts[(size_t)r], Part, st);
         }
         if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
         if (r + 1 == nb) break;
@@ -321,7 +359,7 @@ trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void
             ug.gamma = minus_one;
             {
                 LaunchTimer t(TRSM_KERNEL_UPDATE_GEMM, dt, bsn, n, r0 + bs, 1, st);
-                e = gemm_launch(dt, ug, st);
+                e = gemm_splitk_launch(dt, ug, update_parts[(size_t)r], Part, st);
             }
             if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
             continue;
@@ -347,7 +385,7 @@ trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void
         ug.a_lower = 0;
         {
             LaunchTimer t(TRSM_KERNEL_UPDATE_GEMM, dt, mrest, n, bs, 1, st);
-            e = gemm_launch(dt, ug, st);
+            e = gemm_splitk_launch(dt, ug, update_parts[(size_t)r], Part, st);
         }
         if (e != hipSuccess) return TRSM_STATUS_HIP_ERROR;
     }

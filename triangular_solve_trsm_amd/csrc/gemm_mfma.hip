@@ -51,7 +51,10 @@
 //     after the other: every workgroup gets the same amount of work;
 //   * tiles are mapped so that each XCD (8 per chip, each with its own L2)
 //     works on a band of 8 column tiles at a time, and the workgroups of one
-//     XCD cover roughly 8 x 8 tiles, sharing the A and Bm panels in its L2.
+//     XCD cover roughly 8 x 8 tiles, sharing the A and Bm panels in its L2;
+//   * a product with few output tiles and a long K (a narrow B) can be cut
+//     along K (gemm_splitk_launch): the chunks run as one batched launch
+//     into partial sums, which a reduction kernel adds in a fixed order.
 #include <type_traits>
 
 #include "buffer_ops.h"
@@ -141,6 +144,8 @@ struct GemmParams {
     int tilesM, tilesN;
     int binner;  // batched launches (gridDim.y problems): see GemmDesc
     int64_t sAo, sAi, sBo, sBi, sCo, sCi, sDo, sDi;
+    int64_t sKo;  // triangular A: column offset of problem zo in the triangle
+    int fold;     // triangular A: one workgroup per pair of row tiles
 };
 
 // Workgroup -> tile: consecutive workgroups go round-robin to the 8 XCDs, so
@@ -245,8 +250,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     const int q = lane >> 4;
 
     // triangular A: workgroup w takes row tiles i and tilesM-1-i of one
-    // column tile (their K ranges sum to the same length for every i)
-    const int rowsM = TRI ? (p.tilesM + 1) / 2 : p.tilesM;
+    // column tile (their K ranges sum to the same length for every i).  A
+    // column slice of the triangle (split K) is not folded: most of its row
+    // tiles have the slice's full length.
+    const bool fold = TRI && p.fold;
+    const int rowsM = fold ? (p.tilesM + 1) / 2 : p.tilesM;
     if (blockIdx.x >= (unsigned)(rowsM * p.tilesN)) return;
     // Operands of problem blockIdx.y of a batch.  Kept in locals: `p` is
     // never written, so its fields stay scalar (kernel-argument) loads.
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
 
     // one pass per row tile: tm0, then (triangular A) its partner
     const int tm1 = p.tilesM - 1 - tm0;
-    const int npass = (TRI && tm1 != tm0) ? 2 : 1;
+    const int npass = (fold && tm1 != tm0) ? 2 : 1;
     for (int pass = 0; pass < npass; ++pass) {
         const int tm = pass == 0 ? tm0 : tm1;
         if (pass > 0) __syncthreads();  // the LDS buffers are reused
@@ -272,8 +280,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         const int64_t i0t = CPLX ? i0 / 2 : i0;
         int64_t kend = Kr;
         if (TRI) {
-            const int64_t lim = i0 + MT;  // real rows; K has the same (real) scale
+            // real rows; K has the same (real) scale.  Problem zo of a batch
+            // starts zo*sKo columns right of the triangle's first column.
+            const int64_t koff = (int64_t)zo * p.sKo * (CPLX ? 2 : 1);
+            const int64_t lim = i0 + MT - koff;
             kend = lim < Kr ? lim : Kr;
+            if (kend < 0) kend = 0;
         }
         const int nkt = (int)((kend + KT - 1) / KT);
 
@@ -610,6 +622,8 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
     p.binner = nz > 1 ? (int)g.binner : 1;
     p.sAo = g.sAo; p.sAi = g.sAi; p.sBo = g.sBo; p.sBi = g.sBi;
     p.sCo = g.sCo; p.sCi = g.sCi; p.sDo = g.sDo; p.sDi = g.sDi;
+    p.sKo = nz > 1 && g.a_lower ? g.sKo : 0;
+    p.fold = g.a_lower && p.sKo == 0;
     if (nz > 1) {
         if (g.split != 0 || g.binner < 1) return hipErrorInvalidValue;
         // every problem's operands keep the alignment of the first
@@ -619,7 +633,7 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
         if (!al(g.sCo, g.sCi)) p.c_vec = 0;
         if (!al(g.sDo, g.sDi)) p.d_vec = p.d2_vec = 0;
     }
-    const int64_t rowsM = g.a_lower ? (tM + 1) / 2 : tM;  // triangular: pairs of row tiles
+    const int64_t rowsM = p.fold ? (tM + 1) / 2 : tM;  // folded triangle: pairs of row tiles
     const dim3 grid((unsigned)(rowsM * tN), (unsigned)nz);
     const bool vec = p.a_vec && p.b_vec;
     if (g.a_lower) {
@@ -661,7 +675,98 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
     return launch_tile<T, 64, 32, KT>(g, st);  // batched: the small products of the inversion
 }
 
+// ---- split K: the reduction of the partial products -----------------------
+template <typename T>
+__device__ __forceinline__ T add_elem(T a, T b) {
+    if constexpr (GemmTraits<T>::kCplx) return T{a.re + b.re, a.im + b.im};
+    else return a + b;
+}
+
+// out(i, j) = gamma * sum_s part_s(i, j) + beta * C(i, j); one column per
+// blockIdx.y, rows across the threads (coalesced over every operand).
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    int64_t M, int parts, const T *__restrict__ part, int64_t pstride, const T *__restrict__ C,
+    int64_t ldc, T *__restrict__ D, int64_t ldd, T *__restrict__ D2, int64_t ldd2, int64_t split,
+    Scalar beta, Scalar gamma, int has_c) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= M) return;
+    const int64_t j = blockIdx.y;
+    const T *src = part + i + j * M;
+    T s = src[0];
+    for (int t = 1; t < parts; ++t) s = add_elem<T>(s, src[t * pstride]);
+    T out = Elem<T>::mul(Elem<T>::from(gamma), s);
+    if (has_c) out = add_elem<T>(out, Elem<T>::mul(Elem<T>::from(beta), C[i + j * ldc]));
+    if (i < split) D2[i + j * ldd2] = out;
+    else D[i + j * ldd] = out;
+}
+
+template <typename T>
+hipError_t splitk_reduce_t(const GemmDesc &g, int parts, const void *partial, hipStream_t st) {
+    const int64_t gx = (g.M + 255) / 256;
+    if (g.N > 65535 || gx > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const int has_c = (g.C != nullptr) && (g.beta.re != 0.0 || g.beta.im != 0.0);
+    T *D = static_cast<T *>(g.D);
+    T *D2 = g.D2 ? static_cast<T *>(g.D2) : D;
+    hipLaunchKernelGGL((splitk_reduce_kernel<T>), dim3((unsigned)gx, (unsigned)g.N), dim3(256), 0,
+                       st, g.M, parts, static_cast<const T *>(partial), g.M * g.N,
+                       static_cast<const T *>(g.C), g.ldc, D, g.ldd, D2,
+                       g.D2 ? g.ldd2 : g.ldd, g.D2 ? g.split : (int64_t)0, g.beta, g.gamma, has_c);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+int gemm_splitk_parts(int dtype, int64_t M, int64_t N, int64_t K, int64_t target_workgroups) {
+    if (M <= 0 || N <= 0 || K <= 0 || target_workgroups <= 0) return 1;
+    const int64_t Mr = (dtype == C64F || dtype == C32F) ? 2 * M : M;
+    const int64_t tiles = ((Mr + 63) / 64) * ((N + 31) / 32);
+    int64_t parts = 1;
+    while (2 * parts * tiles <= target_workgroups && K % (2 * parts * kSplitKMinChunk) == 0 &&
+           2 * parts * M * N <= kSplitKMaxElems)
+        parts *= 2;
+    return (int)parts;
+}
+
+hipError_t gemm_splitk_launch(int dtype, const GemmDesc &g, int parts, void *partial,
+                              hipStream_t stream) {
+    if (parts <= 1) return gemm_launch(dtype, g, stream);
+    if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    if (g.batch > 1 || g.K % parts != 0 || partial == nullptr ||
+        (int64_t)parts * g.M * g.N > kSplitKMaxElems)
+        return hipErrorInvalidValue;
+    const int64_t kc = g.K / parts;
+    GemmDesc c{};
+    c.M = g.M;
+    c.N = g.N;
+    c.K = kc;
+    c.A = g.A;
+    c.lda = g.lda;
+    c.Bm = g.Bm;
+    c.ldb = g.ldb;
+    c.C = nullptr;
+    c.ldc = g.M;
+    c.D = partial;
+    c.ldd = g.M;
+    c.beta = Scalar{0.0, 0.0};
+    c.gamma = Scalar{1.0, 0.0};
+    c.a_lower = g.a_lower;
+    c.batch = parts;
+    c.binner = 1;
+    c.sAo = kc * g.lda;  // chunk s: columns [s*kc, (s+1)*kc) of A
+    c.sBo = kc;          //          rows [s*kc, (s+1)*kc) of Bm
+    c.sDo = g.M * g.N;
+    c.sKo = kc;          // triangular A: chunk s skips the K tiles right of the diagonal
+    hipError_t e = gemm_launch(dtype, c, stream);
+    if (e != hipSuccess) return e;
+    switch (dtype) {
+        case R32F: return splitk_reduce_t<float>(g, parts, partial, stream);
+        case R64F: return splitk_reduce_t<double>(g, parts, partial, stream);
+        case C64F: return splitk_reduce_t<cplx>(g, parts, partial, stream);
+        case C32F: return splitk_reduce_t<cplx32>(g, parts, partial, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t gemm_launch(int dtype, const GemmDesc &g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;

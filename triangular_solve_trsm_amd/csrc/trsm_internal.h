@@ -60,7 +60,10 @@ hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t 
 // K-tiles to the right of a row tile's diagonal are skipped (requires M == K).
 // batch > 1: `batch` independent problems of the same shape; problem
 // z = zo * binner + zi (0 <= zi < binner) finds its operands at element
-// offsets zo * s?o + zi * s?i from the pointers (split must be 0).  A
+// offsets zo * s?o + zi * s?i from the pointers (split must be 0).  With
+// a_lower, problem z's A is the column slice that starts zo * sKo columns
+// into the triangle: its element (i, k) is zero (explicitly stored) when
+// k + zo * sKo > i, and the K-tiles wholly in that part are skipped.  A
 // value-initialised descriptor (batch 0) is a single problem.
 struct GemmDesc {
     int64_t M, N, K;
@@ -79,8 +82,28 @@ struct GemmDesc {
     int a_lower;
     int64_t batch, binner;
     int64_t sAo, sAi, sBo, sBi, sCo, sCi, sDo, sDi;
+    int64_t sKo;
 };
 hipError_t gemm_launch(int dtype, const GemmDesc &g, hipStream_t stream);
+
+// Split-K form of a single (batch <= 1) product, for products with few
+// output tiles and a long K, whose few workgroups would each walk the whole
+// K range: the K range is cut into `parts` equal chunks, computed by one
+// batched launch into `partial` (parts column-major M x N blocks, ld M),
+// then D = beta * C + gamma * sum_s partial_s (s ascending, so the result
+// does not depend on timing) by a reduction kernel that keeps gemm_launch's
+// D/D2 row split.  With a_lower each chunk still skips the K tiles right of
+// the diagonal (sKo = chunk length), so a triangular product keeps its
+// halved arithmetic.  parts == 1 is plain gemm_launch.
+// gemm_splitk_parts picks parts: a power of two with chunks of at least
+// kSplitKMinChunk (a multiple of it) and at most target_workgroups tiles of
+// 64 x 32 real rows x columns over all chunks; 1 when no split fits.
+// parts * M * N never exceeds kSplitKMaxElems.
+constexpr int64_t kSplitKMinChunk = 128;
+constexpr int64_t kSplitKMaxElems = int64_t(1) << 21;
+int gemm_splitk_parts(int dtype, int64_t M, int64_t N, int64_t K, int64_t target_workgroups);
+hipError_t gemm_splitk_launch(int dtype, const GemmDesc &g, int parts, void *partial,
+                              hipStream_t stream);
 
 // ---- auxiliary kernels ----------------------------------------------------
 // B[p] <- 0 for an m x n column-major matrix per problem.
