@@ -21,7 +21,8 @@
 //      blocks [W11 0; . W22] of one ib block becomes the inverse of the
 //      2b x 2b block [L11 0; L21 L22] through its lower-left block
 //      X21 = -W22 L21 W11, two batched GEMMs per level (W22 L21 with the
-//      triangular A path, then -(W22 L21) W11).
+//      triangular A path, then -(W22 L21) W11 with the triangular Bm path:
+//      both skip the zero half of their triangular factor).
 //
 // Substitution kernel, gfx950 mapping (one wavefront per workgroup, no
 // barriers):
@@ -39,8 +40,9 @@
 //     one column ahead is far less than the memory latency.  LDS is not used.
 // Everything above the diagonal of each ib x ib block of W is written as an
 // explicit zero (the substitution tile's own upper part, and the columns
-// right of it inside the ib block): the doubling step reads W11 as a full
-// operand, and the triangular GEMM of the solve phase relies on the zeros.
+// right of it inside the ib block): the doubling step's products and the
+// triangular GEMM of the solve phase skip only whole zero K tiles and rely
+// on the zeros inside the tiles they do read.
 #include "buffer_ops.h"
 #include "scalar_ops.h"
 
@@ -290,6 +292,7 @@ hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t 
             g2.ldd2 = ib;
             g2.beta = zero;
             g2.gamma = minus_one;
+            g2.b_lower = 1;
             g2.batch = nfull;
             g2.binner = pp;
             g2.sAo = pp * b * b;
@@ -334,6 +337,7 @@ hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t 
             g2.ldd2 = ib;
             g2.beta = zero;
             g2.gamma = minus_one;
+            g2.b_lower = 1;
             if ((e = gemm_launch(dtype, g2, stream)) != hipSuccess) return e;
         }
     }

@@ -211,7 +211,10 @@ __device__ __forceinline__ void store_rows4(R *X, int64_t ld, int64_t lim, int64
 // that the solve and the update appear as distinct kernels in traces.
 // VEC: A and Bm columns are 16-byte aligned (16-byte loads); otherwise the
 // loads are split into dwords.
-template <typename T, int MT, int NT, int KT, bool TRI, bool VEC>
+// BLO: Bm is lower triangular (explicit zeros above its diagonal), as the
+// right factor of the inversion's second product: a column tile starting at
+// column j0 skips the K tiles wholly above row j0.
+template <typename T, int MT, int NT, int KT, bool TRI, bool VEC, bool BLO = false>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     using Tr = GemmTraits<T>;
     using R = typename Tr::R;
@@ -287,7 +290,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
             kend = lim < Kr ? lim : Kr;
             if (kend < 0) kend = 0;
         }
-        const int nkt = (int)((kend + KT - 1) / KT);
+        // lower-triangular Bm: its rows above j0 are zero in this column tile
+        const int ktb = BLO ? (int)((CPLX ? 2 * j0 : j0) / KT) : 0;
+        const int nkt = (int)((kend + KT - 1) / KT) - ktb;
 
         // ---- accumulators start at sc * C ----------------------------------
         Acc acc[FM][FN];
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         // after issuing them, before the MFMAs they are meant to overlap.
         auto load_tiles = [&](int kt, auto set_c) {
             constexpr int S = decltype(set_c)::value;
-            const int64_t k0 = (int64_t)kt * KT;  // real k offset
+            const int64_t k0 = (int64_t)(kt + ktb) * KT;  // real k offset
             const int64_t k0t = CPLX ? k0 / 2 : k0;
             {
                 const int64_t off = i0t + k0t * p.lda;
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         // zero (only the last, ragged K tile has any: a uniform test first).
         auto store_tiles = [&](int buf, int kt, auto set_c) {
             constexpr int S = decltype(set_c)::value;
-            const int64_t k0 = (int64_t)kt * KT;
+            const int64_t k0 = (int64_t)(kt + ktb) * KT;
             const int64_t k0t = CPLX ? k0 / 2 : k0;
             const bool ragged = k0 + KT > Kr;  // wave-uniform
 #pragma unroll
@@ -636,7 +641,14 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
     const int64_t rowsM = p.fold ? (tM + 1) / 2 : tM;  // folded triangle: pairs of row tiles
     const dim3 grid((unsigned)(rowsM * tN), (unsigned)nz);
     const bool vec = p.a_vec && p.b_vec;
-    if (g.a_lower) {
+    if (g.b_lower) {
+        if constexpr (MT == 64 && NT == 32) {  // the only shape launched with it
+            if (vec) hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, false, true, true>), grid, dim3(256), 0, st, p);
+            else hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, false, false, true>), grid, dim3(256), 0, st, p);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    } else if (g.a_lower) {
         if (vec) hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, true, true>), grid, dim3(256), 0, st, p);
         else hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, true, false>), grid, dim3(256), 0, st, p);
     } else {
@@ -661,7 +673,7 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
 // waves per CU to cover its loads; it lost on every shape measured.
 template <typename T, int KT>
 hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
-    if (g.a_lower) return launch_tile<T, 64, 32, KT>(g, st);
+    if (g.a_lower || g.b_lower) return launch_tile<T, 64, 32, KT>(g, st);
     if (g.batch <= 1) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
         if constexpr (GemmTraits<T>::kCplx) {
@@ -770,6 +782,7 @@ hipError_t gemm_splitk_launch(int dtype, const GemmDesc &g, int parts, void *par
 
 hipError_t gemm_launch(int dtype, const GemmDesc &g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
+    if (g.a_lower && g.b_lower) return hipErrorInvalidValue;
     // 32-bit buffer offsets inside one K tile of A and one column tile of Bm
     const int64_t es = (int64_t)dtype_size(dtype);
     if (g.lda * es * 32 + 4096 > 0x7fffffffLL || g.ldb * es * 128 + 4096 > 0x7fffffffLL)

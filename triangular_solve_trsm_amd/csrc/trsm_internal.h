@@ -58,6 +58,8 @@ hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t 
 // C may alias D (in place).  beta == 0 means C is not read (may be null).
 // a_lower != 0: A is lower triangular (explicit zeros above the diagonal);
 // K-tiles to the right of a row tile's diagonal are skipped (requires M == K).
+// b_lower != 0: Bm is lower triangular (explicit zeros above the diagonal);
+// the K-tiles above a column tile's diagonal are skipped.  Not with a_lower.
 // batch > 1: `batch` independent problems of the same shape; problem
 // z = zo * binner + zi (0 <= zi < binner) finds its operands at element
 // offsets zo * s?o + zi * s?i from the pointers (split must be 0).  With
@@ -80,6 +82,7 @@ struct GemmDesc {
     int64_t split;
     Scalar beta, gamma;
     int a_lower;
+    int b_lower;
     int64_t batch, binner;
     int64_t sAo, sAi, sBo, sBi, sCo, sCi, sDo, sDi;
     int64_t sKo;
