@@ -192,8 +192,6 @@ trsm_status_t check_args(int dt, int64_t m, int64_t n, const void *alpha, const 
 trsm_status_t hip_status(hipError_t e) { return e == hipSuccess ? TRSM_STATUS_SUCCESS : TRSM_STATUS_HIP_ERROR; }
 
 // Left-looking once an update has this many 64 x 64 tiles (four per CU).
-constexpr int64_t kLeftMinTiles = 1024;
-
 bool valid_ib(int ib) { return ib == 64 || ib == 128 || ib == 256 || ib == 512 || ib == 1024; }
 
 // Nearest tabulated problem for this data type (section 4.3.2: online
@@ -221,17 +219,15 @@ int select_ib(int dt, int64_t m, int64_t n) { return select_entry(dt, m, n).ib; 
 // block row r+1 is updated once, by all solved rows, with K = (r+1)*ib.
 // Right-looking (each solved block row updates every row below it, M = rows
 // left) does the same arithmetic in another order.  The offline sweep
-// records which one measured faster for each (data type, order); a left-
-// looking update has only ib rows, so a narrow B, which gives it too few
-// tiles, stays right-looking.  TRSM_SCHEDULE=left|right overrides both
-// (tuning and tests).
-bool use_left_looking(int dt, int64_t m, int64_t n, int ib, bool table_left) {
+// records which one measured faster for each (data type, m, n); a
+// left-looking update of a narrow B has few output tiles and a long K, which
+// split K (below) turns into enough workgroups.  TRSM_SCHEDULE=left|right
+// overrides the table (tuning and tests).
+bool use_left_looking(bool table_left) {
     const char *e = std::getenv("TRSM_SCHEDULE");
     if (e && std::strcmp(e, "left") == 0) return true;
     if (e && std::strcmp(e, "right") == 0) return false;
-    if (!table_left) return false;
-    const int64_t rows = (dt == C64F || dt == C32F ? 2 : 1) * (int64_t)(ib < m ? ib : m);  // real rows
-    return ((rows + 63) / 64) * ((n + 63) / 64) >= kLeftMinTiles;
+    return table_left;
 }
 
 // Split-K target for phase 2: a product with so few 64 x 32 tiles that
@@ -255,7 +251,7 @@ int64_t splitk_target() {
 trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void *A,
                           int64_t lda, void *B, int64_t ldb, int ib, bool table_left, int dev,
                           hipStream_t st) {
-    const bool left = use_left_looking(dt, m, n, ib, table_left);
+    const bool left = use_left_looking(table_left);
     const size_t es = dtype_size(dt);
     const int64_t nb = (m + ib - 1) / ib;
     size_t wbytes = (size_t)nb * ib * ib * es;
