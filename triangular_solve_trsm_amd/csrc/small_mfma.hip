@@ -12,7 +12,10 @@
 // blocked algorithm at 16 x 16 granularity inside one workgroup:
 //
 //   * the lower 16 x 16 blocks of L (ten of them, 40 KB for complex) are
-//     staged in LDS; rows past m become identity rows;
+//     staged in LDS; rows past m become identity rows; every element of A
+//     and B moves by a raw buffer operation with no branch around it, so all
+//     of a thread's loads are in flight at once and its stores go out
+//     back to back (guarded loads made the compiler wait for each one);
 //   * one wave inverts the four diagonal blocks in place (lane group g takes
 //     block g) by substitution against the columns of the identity (section
 //     4.3.1's column-streamed inversion at 16 x 16 scale);
@@ -27,6 +30,7 @@
 //     are read.
 // Four waves per workgroup and four workgroups per CU keep sixteen waves
 // per CU, so one workgroup's loads overlap the others' products.
+#include "buffer_ops.h"
 #include "scalar_ops.h"
 
 namespace trsm {
@@ -63,7 +67,37 @@ __device__ __forceinline__ double afrag(const cplx (*Lb)[16], int a, int t, int 
     return sgn * v;
 }
 
+// One element of A through a raw buffer load; `ok == false` reads nothing
+// (an offset past the range returns zero without a memory access).
 template <typename T>
+__device__ __forceinline__ T ld_elem(__amdgpu_buffer_rsrc_t r, int64_t idx, bool ok) {
+    const uint32_t off = ok ? (uint32_t)(idx * (int64_t)sizeof(T)) : 0xfffffff0u;
+    if constexpr (sizeof(T) == 16) {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    } else {
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    }
+}
+
+// One element of B written through a raw buffer store; `ok == false` writes
+// nothing (a store past the range is dropped).
+template <typename T>
+__device__ __forceinline__ void st_elem(__amdgpu_buffer_rsrc_t r, int64_t idx, bool ok, T v) {
+    const uint32_t off = ok ? (uint32_t)(idx * (int64_t)sizeof(T)) : 0xfffffff0u;
+    if constexpr (sizeof(T) == 16) {
+        typedef unsigned u4t __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4t, v), r, off, 0, 0);
+    } else {
+        typedef unsigned u2t __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u2t, v), r, off, 0, 0);
+    }
+}
+
+// BUF: one problem's A and B each span less than 2^31 bytes, so they are
+// read and written with branch-free buffer operations, all in flight
+// together (a guarded access per element makes the compiler wait for each
+// one before the next).
+template <typename T, bool BUF>
 __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64_t ncg,
                                                          Scalar alpha_s, const T *__restrict__ A,
                                                          int64_t lda, int64_t strideA,
@@ -88,18 +122,41 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
     // ---- 1. lower blocks of L into LDS (rows >= m: identity) ---------------
     {
         const int i = tid & 15, k = tid >> 4;
+        if constexpr (BUF) {
+            // all ten loads first, then the masks and the LDS writes
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(Ap, ((int64_t)(m - 1) * lda + m) * (int64_t)sizeof(T));
+            T v[kPanels * (kPanels + 1) / 2];
 #pragma unroll
-        for (int q = 0; q < kPanels; ++q) {
+            for (int q = 0; q < kPanels; ++q)
 #pragma unroll
-            for (int p = 0; p <= q; ++p) {
-                const int gi = 16 * q + i, gk = 16 * p + k;
-                T v = E::zero();
-                if (gi < m && gk < m) {
-                    if (gi >= gk) v = Ap[gi + (int64_t)gk * lda];
-                } else if (gi == gk) {
-                    v = E::one();
+                for (int p = 0; p <= q; ++p) {
+                    const int gi = 16 * q + i, gk = 16 * p + k;
+                    v[blk(q, p)] = ld_elem<T>(rs, gi + (int64_t)gk * lda, gi < m && gk < m && gi >= gk);
                 }
-                Lb[blk(q, p)][k][i] = v;
+#pragma unroll
+            for (int q = 0; q < kPanels; ++q)
+#pragma unroll
+                for (int p = 0; p <= q; ++p) {
+                    const int gi = 16 * q + i, gk = 16 * p + k;
+                    // out-of-range reads came back zero; rows past m get a 1
+                    // on the diagonal
+                    Lb[blk(q, p)][k][i] = E::sel(gi == gk && gi >= m, E::one(), v[blk(q, p)]);
+                }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kPanels; ++q) {
+#pragma unroll
+                for (int p = 0; p <= q; ++p) {
+                    const int gi = 16 * q + i, gk = 16 * p + k;
+                    T v = E::zero();
+                    if (gi < m && gk < m) {
+                        if (gi >= gk) v = Ap[gi + (int64_t)gk * lda];
+                    } else if (gi == gk) {
+                        v = E::one();
+                    }
+                    Lb[blk(q, p)][k][i] = v;
+                }
             }
         }
     }
@@ -130,12 +187,25 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
     const int64_t col = cgi * 64 + w * 16 + c;
     const bool colok = col < n;
     T *__restrict__ Bc = Bp + col * ldb;
+    const __amdgpu_buffer_rsrc_t rsb =
+        make_rsrc(Bp, BUF ? ((n - 1) * ldb + m) * (int64_t)sizeof(T) : 0);
     d4 acc[kPanels][TILES];
 #pragma unroll
     for (int p = 0; p < kPanels; ++p) {
 #pragma unroll
         for (int a = 0; a < TILES; ++a) {
-            if constexpr (CPLX) {
+            if constexpr (BUF && CPLX) {
+                const int r0 = 16 * p + 8 * a + g;
+                const cplx z0 = ld_elem<cplx>(rsb, r0 + col * ldb, colok && r0 < m);
+                const cplx z1 = ld_elem<cplx>(rsb, r0 + 4 + col * ldb, colok && r0 + 4 < m);
+                acc[p][a] = d4{z0.re, z0.im, z1.re, z1.im};
+            } else if constexpr (BUF) {
+                const int r0 = 16 * p + 4 * g;
+                double v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = ld_elem<double>(rsb, r0 + e + col * ldb, colok && r0 + e < m);
+                acc[p][a] = d4{v[0], v[1], v[2], v[3]};
+            } else if constexpr (CPLX) {
                 const int r0 = 16 * p + 8 * a + g;  // complex rows r0 and r0 + 4
                 cplx z0{0.0, 0.0}, z1{0.0, 0.0};
                 if (colok && r0 < m) z0 = Bc[r0];
@@ -167,20 +237,10 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
                     x[a] = __builtin_amdgcn_mfma_f64_16x16x4f64(
                         afrag(Lb[blk(p, p)], a, t, s, c, g, 1.0), acc[p][t][s], x[a], 0, 0, 0);
         }
-        // store alpha * X_p
+        // X_p replaces B_p in the accumulators; the stores wait until the end,
+        // so no panel's products wait for another panel's stores to drain
 #pragma unroll
-        for (int a = 0; a < TILES; ++a) {
-            if constexpr (CPLX) {
-                const int r0 = 16 * p + 8 * a + g;
-                if (colok && r0 < m) Bc[r0] = E::mul(alpha, cplx{x[a][0], x[a][1]});
-                if (colok && r0 + 4 < m) Bc[r0 + 4] = E::mul(alpha, cplx{x[a][2], x[a][3]});
-            } else {
-                const int r0 = 16 * p + 4 * g;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (colok && r0 + e < m) Bc[r0 + e] = alpha * x[a][e];
-            }
-        }
+        for (int a = 0; a < TILES; ++a) acc[p][a] = x[a];
         // update the panels below
 #pragma unroll
         for (int q = p + 1; q < kPanels; ++q) {
@@ -197,6 +257,34 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
         }
         }
     }
+
+    // ---- 5. B <- alpha X ---------------------------------------------------
+#pragma unroll
+    for (int p = 0; p < kPanels; ++p) {
+#pragma unroll
+        for (int a = 0; a < TILES; ++a) {
+            if constexpr (BUF && CPLX) {
+                const int r0 = 16 * p + 8 * a + g;
+                st_elem<cplx>(rsb, r0 + col * ldb, colok && r0 < m, E::mul(alpha, cplx{acc[p][a][0], acc[p][a][1]}));
+                st_elem<cplx>(rsb, r0 + 4 + col * ldb, colok && r0 + 4 < m,
+                              E::mul(alpha, cplx{acc[p][a][2], acc[p][a][3]}));
+            } else if constexpr (BUF) {
+                const int r0 = 16 * p + 4 * g;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    st_elem<double>(rsb, r0 + e + col * ldb, colok && r0 + e < m, alpha * acc[p][a][e]);
+            } else if constexpr (CPLX) {
+                const int r0 = 16 * p + 8 * a + g;
+                if (colok && r0 < m) Bc[r0] = E::mul(alpha, cplx{acc[p][a][0], acc[p][a][1]});
+                if (colok && r0 + 4 < m) Bc[r0 + 4] = E::mul(alpha, cplx{acc[p][a][2], acc[p][a][3]});
+            } else {
+                const int r0 = 16 * p + 4 * g;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (colok && r0 + e < m) Bc[r0 + e] = alpha * acc[p][a][e];
+            }
+        }
+    }
 }
 
 }  // namespace
@@ -209,16 +297,28 @@ hipError_t small_mfma_launch(int dtype, int m, int64_t n, Scalar alpha, const vo
     const int64_t nblk = ncg * batch;
     if (nblk <= 0) return hipSuccess;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    // one problem's A and B in 32-bit buffer offsets (with room for the
+    // past-the-end offset of skipped elements)
+    const int64_t es = dtype == C64F ? 16 : 8;
+    const bool buf = ((int64_t)(m - 1) * lda + m) * es < 0x7fffffffLL &&
+                     (n - 1) <= (0x7fffffffLL / es - m) / (ldb > 0 ? ldb : 1);
+    const dim3 grid((unsigned)nblk);
     switch (dtype) {
         case R64F:
-            hipLaunchKernelGGL((small_mfma_kernel<double>), dim3((unsigned)nblk), dim3(256), 0, stream, m, n,
-                               ncg, alpha, static_cast<const double *>(A), lda, strideA,
-                               static_cast<double *>(B), ldb, strideB);
+            if (buf)
+                hipLaunchKernelGGL((small_mfma_kernel<double, true>), grid, dim3(256), 0, stream, m, n, ncg, alpha,
+                                   static_cast<const double *>(A), lda, strideA, static_cast<double *>(B), ldb, strideB);
+            else
+                hipLaunchKernelGGL((small_mfma_kernel<double, false>), grid, dim3(256), 0, stream, m, n, ncg, alpha,
+                                   static_cast<const double *>(A), lda, strideA, static_cast<double *>(B), ldb, strideB);
             break;
         case C64F:
-            hipLaunchKernelGGL((small_mfma_kernel<cplx>), dim3((unsigned)nblk), dim3(256), 0, stream, m, n,
-                               ncg, alpha, static_cast<const cplx *>(A), lda, strideA,
-                               static_cast<cplx *>(B), ldb, strideB);
+            if (buf)
+                hipLaunchKernelGGL((small_mfma_kernel<cplx, true>), grid, dim3(256), 0, stream, m, n, ncg, alpha,
+                                   static_cast<const cplx *>(A), lda, strideA, static_cast<cplx *>(B), ldb, strideB);
+            else
+                hipLaunchKernelGGL((small_mfma_kernel<cplx, false>), grid, dim3(256), 0, stream, m, n, ncg, alpha,
+                                   static_cast<const cplx *>(A), lda, strideA, static_cast<cplx *>(B), ldb, strideB);
             break;
         default: return hipErrorInvalidValue;
     }
