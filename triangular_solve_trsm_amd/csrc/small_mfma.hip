@@ -28,7 +28,7 @@
 //   * complex fp64 uses the real 2x2 embedding (4 real products per complex
 //     product), expanded from the complex LDS blocks when the A fragments
 //     are read.
-// Four waves per workgroup and four workgroups per CU keep sixteen waves
+// Four waves per workgroup and three (complex) or four (fp64) workgroups
 // per CU, so one workgroup's loads overlap the others' products.
 #include "buffer_ops.h"
 #include "scalar_ops.h"
@@ -119,7 +119,49 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
     T *__restrict__ Bp = B + prob * strideB;
     const int np = (m + 15) >> 4;  // panels that hold rows < m
 
-    // ---- 1. lower blocks of L into LDS (rows >= m: identity) ---------------
+    // ---- 1. this wave's 16 columns, all rows, into accumulators ----------
+    // Issued first: B does not depend on L, so these loads are in flight
+    // while L is staged and inverted (measured faster than loading B after
+    // the inversion, although the longer register life leaves three waves
+    // per SIMD for complex instead of four).
+    const int64_t col = cgi * 64 + w * 16 + c;
+    const bool colok = col < n;
+    T *__restrict__ Bc = Bp + col * ldb;
+    const __amdgpu_buffer_rsrc_t rsb =
+        make_rsrc(Bp, BUF ? ((n - 1) * ldb + m) * (int64_t)sizeof(T) : 0);
+    d4 acc[kPanels][TILES];
+#pragma unroll
+    for (int p = 0; p < kPanels; ++p) {
+#pragma unroll
+        for (int a = 0; a < TILES; ++a) {
+            if constexpr (BUF && CPLX) {
+                const int r0 = 16 * p + 8 * a + g;
+                const cplx z0 = ld_elem<cplx>(rsb, r0 + col * ldb, colok && r0 < m);
+                const cplx z1 = ld_elem<cplx>(rsb, r0 + 4 + col * ldb, colok && r0 + 4 < m);
+                acc[p][a] = d4{z0.re, z0.im, z1.re, z1.im};
+            } else if constexpr (BUF) {
+                const int r0 = 16 * p + 4 * g;
+                double v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = ld_elem<double>(rsb, r0 + e + col * ldb, colok && r0 + e < m);
+                acc[p][a] = d4{v[0], v[1], v[2], v[3]};
+            } else if constexpr (CPLX) {
+                const int r0 = 16 * p + 8 * a + g;  // complex rows r0 and r0 + 4
+                cplx z0{0.0, 0.0}, z1{0.0, 0.0};
+                if (colok && r0 < m) z0 = Bc[r0];
+                if (colok && r0 + 4 < m) z1 = Bc[r0 + 4];
+                acc[p][a] = d4{z0.re, z0.im, z1.re, z1.im};
+            } else {
+                const int r0 = 16 * p + 4 * g;  // rows r0 .. r0 + 3
+                double v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (colok && r0 + e < m) ? Bc[r0 + e] : 0.0;
+                acc[p][a] = d4{v[0], v[1], v[2], v[3]};
+            }
+        }
+    }
+
+    // ---- 2. lower blocks of L into LDS (rows >= m: identity) ---------------
     {
         const int i = tid & 15, k = tid >> 4;
         if constexpr (BUF) {
@@ -162,7 +204,7 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
     }
     __syncthreads();
 
-    // ---- 2. wave 0 inverts the diagonal blocks in place --------------------
+    // ---- 3. wave 0 inverts the diagonal blocks in place --------------------
     // Lane group g takes block g, lane c of it column c of the inverse.  The
     // pivots' reciprocals are computed first (one per lane) and stored over
     // the diagonal, so the substitution itself only multiplies.
@@ -182,44 +224,6 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
         for (int i = 0; i < 16; ++i) D[c][i] = x[i];
     }
     __syncthreads();
-
-    // ---- 3. this wave's 16 columns, all rows, into accumulators ----------
-    const int64_t col = cgi * 64 + w * 16 + c;
-    const bool colok = col < n;
-    T *__restrict__ Bc = Bp + col * ldb;
-    const __amdgpu_buffer_rsrc_t rsb =
-        make_rsrc(Bp, BUF ? ((n - 1) * ldb + m) * (int64_t)sizeof(T) : 0);
-    d4 acc[kPanels][TILES];
-#pragma unroll
-    for (int p = 0; p < kPanels; ++p) {
-#pragma unroll
-        for (int a = 0; a < TILES; ++a) {
-            if constexpr (BUF && CPLX) {
-                const int r0 = 16 * p + 8 * a + g;
-                const cplx z0 = ld_elem<cplx>(rsb, r0 + col * ldb, colok && r0 < m);
-                const cplx z1 = ld_elem<cplx>(rsb, r0 + 4 + col * ldb, colok && r0 + 4 < m);
-                acc[p][a] = d4{z0.re, z0.im, z1.re, z1.im};
-            } else if constexpr (BUF) {
-                const int r0 = 16 * p + 4 * g;
-                double v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = ld_elem<double>(rsb, r0 + e + col * ldb, colok && r0 + e < m);
-                acc[p][a] = d4{v[0], v[1], v[2], v[3]};
-            } else if constexpr (CPLX) {
-                const int r0 = 16 * p + 8 * a + g;  // complex rows r0 and r0 + 4
-                cplx z0{0.0, 0.0}, z1{0.0, 0.0};
-                if (colok && r0 < m) z0 = Bc[r0];
-                if (colok && r0 + 4 < m) z1 = Bc[r0 + 4];
-                acc[p][a] = d4{z0.re, z0.im, z1.re, z1.im};
-            } else {
-                const int r0 = 16 * p + 4 * g;  // rows r0 .. r0 + 3
-                double v[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (colok && r0 + e < m) ? Bc[r0 + e] : 0.0;
-                acc[p][a] = d4{v[0], v[1], v[2], v[3]};
-            }
-        }
-    }
 
     // ---- 4. X_p = W_p B_p, B_q -= L_qp X_p --------------------------------
     const T alpha = E::from(alpha_s);
