@@ -171,6 +171,28 @@ def test_split_k_phase2(T, dtype, schedule, splitk, n, monkeypatch):
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("schedule", ["left", "right"])
+def test_split_k_odd_leading_dimensions(T, dtype, schedule, monkeypatch):
+    """Split K with lda = m + 3 and ldb = m + 1: columns that are not
+    16-byte aligned take the dword load path, the reduction writes through
+    the odd ldb, A's NaN upper triangle and padding stay unread and B's
+    padding rows untouched."""
+    monkeypatch.setenv("TRSM_SCHEDULE", schedule)
+    monkeypatch.setenv("TRSM_SPLITK", "65536")
+    m, n = 1100, 40
+    L, B = make_problem(dtype, m, n, seed=1100, lda=m + 3, ldb=m + 1, upper="nan")
+    Ad = to_dev(L, pad=np.nan)
+    Bd = to_dev(B, pad=777.0)
+    T.trsm_lln_ex(Ad, Bd, 1.0, ib=256)
+    sync()
+    import torch
+    full = from_dev(torch.as_strided(Bd, (ld_of(B), n), (1, ld_of(B))))
+    assert np.all(full[m:] == 777.0), "padding rows of B were modified"
+    Lz, _ = make_problem(dtype, m, n, seed=1100)
+    check(dtype, full[:m], oracle.solve(Lz, np.asfortranarray(B), 1.0), f"{dtype} {schedule} odd ld")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
+@pytest.mark.parametrize("schedule", ["left", "right"])
 def test_split_k_bidiagonal_exact(T, dtype, schedule, monkeypatch):
     """The running-sum problem stays exact when K is split: every partial sum
     is a small integer, so the reduction of the chunks is exact too."""
