@@ -191,6 +191,26 @@ def test_split_k_odd_leading_dimensions(T, dtype, schedule, monkeypatch):
     check(dtype, full[:m], oracle.solve(Lz, np.asfortranarray(B), 1.0), f"{dtype} {schedule} odd ld")
 
 
+@pytest.mark.parametrize("dtype", ["f64", "c32"])
+def test_split_k_wide_b_keeps_unsplit_products(T, dtype, monkeypatch):
+    """m = 272 at ib = 256, right-looking, n = 65536: the update of the last
+    16 rows (K = 256) fits the partial-sum bound at two chunks, but the
+    reduction's grid takes at most 65535 columns, so a large split-K target
+    must leave it whole.  Checked on sampled columns (independent
+    problems)."""
+    import torch
+    monkeypatch.setenv("TRSM_SCHEDULE", "right")
+    monkeypatch.setenv("TRSM_SPLITK", "1000000")
+    m, n = 272, 65536
+    L, B = make_problem(dtype, m, n, seed=65536)
+    Ad, Bd = to_dev(L), to_dev(B)
+    T.trsm_lln_ex(Ad, Bd, 1.0, ib=256)
+    sync()
+    cols = np.array([0, 1, 31, 32, 32767, 65534, 65535])
+    Xs = from_dev(Bd[:, torch.as_tensor(cols, device=Bd.device)])
+    check(dtype, Xs, oracle.solve(L, np.asfortranarray(B[:, cols]), 1.0), f"{dtype} n=65536")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("schedule", ["left", "right"])
 def test_split_k_bidiagonal_exact(T, dtype, schedule, monkeypatch):

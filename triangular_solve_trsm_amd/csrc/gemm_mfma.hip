@@ -730,7 +730,8 @@ hipError_t splitk_reduce_t(const GemmDesc &g, int parts, const void *partial, hi
 }  // namespace
 
 int gemm_splitk_parts(int dtype, int64_t M, int64_t N, int64_t K, int64_t target_workgroups) {
-    if (M <= 0 || N <= 0 || K <= 0 || target_workgroups <= 0) return 1;
+    // the reduction puts one column per grid row (at most 65535)
+    if (M <= 0 || N <= 0 || N > 65535 || K <= 0 || target_workgroups <= 0) return 1;
     const int64_t Mr = (dtype == C64F || dtype == C32F) ? 2 * M : M;
     const int64_t tiles = ((Mr + 63) / 64) * ((N + 31) / 32);
     int64_t parts = 1;

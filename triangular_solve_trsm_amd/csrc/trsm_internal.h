@@ -100,7 +100,8 @@ hipError_t gemm_launch(int dtype, const GemmDesc &g, hipStream_t stream);
 // halved arithmetic.  parts == 1 is plain gemm_launch.
 // gemm_splitk_parts picks parts: a power of two with chunks of at least
 // kSplitKMinChunk (a multiple of it) and at most target_workgroups tiles of
-// 64 x 32 real rows x columns over all chunks; 1 when no split fits.
+// 64 x 32 real rows x columns over all chunks; 1 when no split fits or
+// N > 65535.
 // parts * M * N never exceeds kSplitKMaxElems.
 constexpr int64_t kSplitKMinChunk = 128;
 constexpr int64_t kSplitKMaxElems = int64_t(1) << 21;
