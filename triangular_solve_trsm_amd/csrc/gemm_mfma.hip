@@ -358,13 +358,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         // the registers are written to LDS (store_tiles), not here: a select on
         // the loaded values would make the compiler wait for the loads right
         // after issuing them, before the MFMAs they are meant to overlap.
-        auto load_tiles = [&](int kt, auto set_c) {
+        // A tile past the last one (live == false) is still issued, on an
+        // empty range: its loads touch no memory and return zero.  Issuing
+        // the same loads on every path lets the compiler wait for exactly the
+        // tile it stores next; with the prefetch under a branch it waited for
+        // every load in flight, the prefetch just issued included.
+        auto load_tiles = [&](int kt, auto set_c, bool live = true) {
             constexpr int S = decltype(set_c)::value;
             const int64_t k0 = (int64_t)(kt + ktb) * KT;  // real k offset
             const int64_t k0t = CPLX ? k0 / 2 : k0;
             {
                 const int64_t off = i0t + k0t * p.lda;
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc(pA + off, (p.extA - off) * (int64_t)sizeof(T));
+                const __amdgpu_buffer_rsrc_t rs =
+                    make_rsrc(pA + off, live ? (p.extA - off) * (int64_t)sizeof(T) : 0);
 #pragma unroll
                 for (int s = 0; s < A_PASSES; ++s) {
                     const int flat = s * 256 + tid;
@@ -376,7 +382,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
             }
             {
                 const int64_t off = k0t + j0 * p.ldb;
-                const __amdgpu_buffer_rsrc_t rs = make_rsrc(pB + off, (p.extB - off) * (int64_t)sizeof(T));
+                const __amdgpu_buffer_rsrc_t rs =
+                    make_rsrc(pB + off, live ? (p.extB - off) * (int64_t)sizeof(T) : 0);
 #pragma unroll
                 for (int s = 0; s < B_PASSES; ++s) {
                     const int flat = s * 256 + tid;
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         if (nkt > 0) {
             if constexpr (DEPTH == 2) {
                 load_tiles(0, I0{});
-                if (nkt > 1) load_tiles(1, I1{});
+                load_tiles(1, I1{}, nkt > 1);
                 store_tiles(0, 0, I0{});
                 __syncthreads();
                 // step kt (kt % 2 == S): set S held tile kt (already in LDS)
@@ -488,7 +495,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
                 auto step = [&](int kt, auto set_c) {
                     constexpr int S = decltype(set_c)::value;
                     using IN = std::integral_constant<int, S ^ 1>;
-                    if (kt + 2 < nkt) load_tiles(kt + 2, set_c);
+                    load_tiles(kt + 2, set_c, kt + 2 < nkt);
                     mfma_tile(S);
                     if (kt + 1 < nkt) {
                         store_tiles(S ^ 1, kt + 1, IN{});
