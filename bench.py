@@ -96,6 +96,33 @@ def summarize_kernels(records):
     return out
 
 
+def update_tiles(records):
+    """Macro tile of each fp64 update launch, by the library's rule for a
+    single real fp64 product (launch_sized in gemm_mfma.hip): 128 x 64 when
+    that gives at least 2048 tiles, 64 x 32 when 64 x 64 gives fewer than
+    1024, 64 x 64 otherwise."""
+    counts = {}
+    for r in records:
+        if r["kind"] != "update_gemm" or r["dtype"] != 1:
+            continue
+        M, N = r["m"], r["n"]
+        if -(-M // 128) * -(-N // 64) >= 2048:
+            t = "128x64"
+        elif -(-M // 64) * -(-N // 64) < 1024:
+            t = "64x32"
+        else:
+            t = "64x64"
+        counts[t] = counts.get(t, 0) + 1
+    return counts
+
+
+def phase2_order(records):
+    """Which phase-2 order the fp64 solve ran: right-looking updates all have
+    K = ib, left-looking ones a K that grows by ib per block row."""
+    ks = {r["k"] for r in records if r["kind"] == "update_gemm" and r["dtype"] == 1}
+    return "right-looking" if len(ks) <= 1 else "left-looking"
+
+
 def cpu_baseline(big, small, seconds=12.0):
     """Time the oracle (as it stands) on a bounded sample of each workload:
     about seconds/2 on a block of right-hand-side columns of the large solve
@@ -257,7 +284,9 @@ def main():
 
     roofline = {
         "bound": "mfma",
-        "kernel": "update_gemm_f64 (gemm_kernel<double,128,64,16>; 64x64 for the last small updates)",
+        "kernel": "update_gemm_f64 (gemm_kernel<double, tile, 16>, launches per tile: "
+                  + ", ".join(f"{t} x{c // args.steps}" for t, c in sorted(update_tiles(recs).items()))
+                  + f" per step; {phase2_order(recs)} phase 2)",
         "achieved": upd.get("tflops"),
         "peak": PEAK["fp64_mfma_tflops"],
         "unit": "TFLOP/s",

@@ -348,9 +348,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
         // Register staging sets: with DEPTH 2 the loads of tile kt+2 are in
         // flight while tile kt+1 waits in the other set, so a load has two
         // tiles of products to arrive.  Small tiles run few products per K
-        // tile and need that; the 128-row tiles keep one set (their register
-        // budget decides how many waves a SIMD holds).
-        constexpr int DEPTH = (MT * NT <= 64 * 64) ? 2 : 1;
+        // tile and need that.  The fp64 128 x 64 tile keeps one set: a second
+        // one takes it from 168 to 194 VGPRs, three waves per SIMD to two,
+        // and measured slower (fp64 8192^2 9.77 -> 9.80 ms).  The complex
+        // 64 x 128 tile stays at three waves with two sets and gains
+        // (complex 8192 x 2048 9.83 -> 9.55 ms; complex fp32 5.06 -> 4.85).
+        constexpr int DEPTH = (MT * NT <= 64 * 64 || CPLX) ? 2 : 1;
         u4v ra[DEPTH][A_PASSES];
         u4v rb[DEPTH][B_PASSES];
 
