@@ -5,7 +5,7 @@
   standard rounding bound of a K-term dot product:
       |D - D_ref| <= 2 (K + 2) u (|beta| |C| + |gamma| |A| |Bm|)   (per element)
   on ragged shapes, odd leading dimensions, the split routing to D2, the
-  triangular skip, both macro-tile sizes, K = 0 and gamma = 0.
+  triangular skip, every macro-tile size, K = 0 and gamma = 0.
 * trsm_kernel_diag_inv (phase 1) against the oracle solving each diagonal
   block against the columns of the identity, which is the definition of the
   inverse the pages build the kernel on (section 4.3.1, the identity tile
@@ -104,6 +104,14 @@ def test_gemm_large_tile_path(T, dtype):
     M = 1450 if dtype in CPLX else 2900
     gemm_case(T, dtype, M, 2900, 45, 1.0, -1.0, seed=3)
     gemm_case(T, dtype, M, 2900, 40, 0.0, 1.0, seed=4, ldpad=3)
+
+
+def test_gemm_fp64_128x128_tile(T):
+    """fp64 products with at least 512 tiles of 128 x 128 and 16-byte
+    aligned operands take the 128 x 128 tile: ragged M and N (2900), even K
+    with a ragged last K tile (46, 302), beta 0 and 1."""
+    gemm_case(T, "f64", 2900, 2900, 46, 1.0, -1.0, seed=5)
+    gemm_case(T, "f64", 2900, 2900, 302, 0.0, 0.5, seed=6)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
