@@ -56,33 +56,40 @@ __global__ __launch_bounds__(256) void transform_kernel(int64_t R, int64_t C,
                                                         int unit) {
     __shared__ T tile[32][33];
     const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
-    const int64_t i0 = (int64_t)blockIdx.x * 32, j0 = (int64_t)blockIdx.y * 32;
-    if (lower && i0 + 31 < j0) return;  // tile wholly above the diagonal (uniform)
+    const int64_t i0 = (int64_t)blockIdx.x * 32;
     auto wanted = [&](int64_t i, int64_t j) { return i < R && j < C && (!lower || i >= j); };
     auto put = [&](int64_t i, int64_t j, T v) {
         dst[i + j * ldd] = (unit && i == j) ? Elem<T>::one() : conj_if<T>(v, conj);
     };
-    if (!trans) {
+    // column tiles in a grid-stride loop: gridDim.y is capped at 65535, and
+    // every thread of the block runs the same iterations (uniform bounds)
+    const int64_t ntj = (C + 31) / 32;
+    for (int64_t jt = blockIdx.y; jt < ntj; jt += gridDim.y) {
+        const int64_t j0 = jt * 32;
+        if (lower && i0 + 31 < j0) break;  // this and later tiles lie above the diagonal
+        if (!trans) {
+            for (int jj = ty; jj < 32; jj += 8) {
+                const int64_t i = i0 + tx, j = j0 + jj;
+                if (!wanted(i, j)) continue;
+                const int64_t a = revR ? R - 1 - i : i, b = revC ? C - 1 - j : j;
+                put(i, j, (unit && i == j) ? Elem<T>::one() : src[a + b * lds]);
+            }
+            continue;
+        }
+        // read src(b, a) with consecutive threads on consecutive b (src rows)
+        for (int ii = ty; ii < 32; ii += 8) {
+            const int64_t i = i0 + ii, j = j0 + tx;
+            if (wanted(i, j) && !(unit && i == j)) {
+                const int64_t a = revR ? R - 1 - i : i, b = revC ? C - 1 - j : j;
+                tile[ii][tx] = src[b + a * lds];
+            }
+        }
+        __syncthreads();
         for (int jj = ty; jj < 32; jj += 8) {
             const int64_t i = i0 + tx, j = j0 + jj;
-            if (!wanted(i, j)) continue;
-            const int64_t a = revR ? R - 1 - i : i, b = revC ? C - 1 - j : j;
-            put(i, j, (unit && i == j) ? Elem<T>::one() : src[a + b * lds]);
+            if (wanted(i, j)) put(i, j, tile[tx][jj]);
         }
-        return;
-    }
-    // read src(b, a) with consecutive threads on consecutive b (src rows)
-    for (int ii = ty; ii < 32; ii += 8) {
-        const int64_t i = i0 + ii, j = j0 + tx;
-        if (wanted(i, j) && !(unit && i == j)) {
-            const int64_t a = revR ? R - 1 - i : i, b = revC ? C - 1 - j : j;
-            tile[ii][tx] = src[b + a * lds];
-        }
-    }
-    __syncthreads();
-    for (int jj = ty; jj < 32; jj += 8) {
-        const int64_t i = i0 + tx, j = j0 + jj;
-        if (wanted(i, j)) put(i, j, tile[tx][jj]);
+        __syncthreads();  // the tile is reused by the next column tile
     }
 }
 
@@ -116,8 +123,9 @@ template <typename T>
 hipError_t transform_t(int64_t R, int64_t C, const void *src, int64_t lds, void *dst, int64_t ldd,
                        const Reflect &f, hipStream_t st) {
     if (R <= 0 || C <= 0) return hipSuccess;
-    const int64_t gx = (R + 31) / 32, gy = (C + 31) / 32;
-    if (gx > 0x7fffffffLL || gy > 65535) return hipErrorInvalidConfiguration;
+    const int64_t gx = (R + 31) / 32;
+    const int64_t gy = (C + 31) / 32 < 65535 ? (C + 31) / 32 : 65535;  // the kernel strides over the rest
+    if (gx > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((transform_kernel<T>), dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, st, R,
                        C, static_cast<const T *>(src), lds, static_cast<T *>(dst), ldd, f.revR,
                        f.revC, f.trans, f.conj, f.lower, f.unit);

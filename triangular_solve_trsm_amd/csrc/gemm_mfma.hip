@@ -696,8 +696,9 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
         } else if constexpr (sizeof(T) == 8) {
             // (16-byte aligned operands only: the dword-load form needs
             // all 256 VGPRs and runs one wave per SIMD)
-            if (((Mr + 127) / 128) * ((g.N + 127) / 128) >= 512 && aligned16(g.A, g.lda, sizeof(T)) &&
-                aligned16(g.Bm, g.ldb, sizeof(T)))
+            // (and more than 64 rows, which a 64-row tile already covers)
+            if (Mr > 64 && ((Mr + 127) / 128) * ((g.N + 127) / 128) >= 512 &&
+                aligned16(g.A, g.lda, sizeof(T)) && aligned16(g.Bm, g.ldb, sizeof(T)))
                 return launch_tile<T, 128, 128, KT>(g, st);
             if (((Mr + 127) / 128) * ((g.N + 63) / 64) >= 2048) return launch_tile<T, 128, 64, KT>(g, st);
         }
