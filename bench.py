@@ -99,7 +99,8 @@ def summarize_kernels(records):
 def update_tiles(records):
     """Macro tile of each fp64 update launch, by the library's rule for a
     single real fp64 product with 16-byte aligned operands (launch_sized in
-    gemm_mfma.hip): 128 x 128 when M > 64 and that gives at least 512 tiles, 128 x 64
+    gemm_mfma.hip): 128 x 128 when M > 64 and that gives at least 512 tiles
+    in rounds of 512 at least 3/4 full, 128 x 64
     when that gives at least 2048, 64 x 32 when 64 x 64 gives fewer than
     1024, 64 x 64 otherwise."""
     counts = {}
@@ -107,7 +108,8 @@ def update_tiles(records):
         if r["kind"] != "update_gemm" or r["dtype"] != 1:
             continue
         M, N = r["m"], r["n"]
-        if M > 64 and -(-M // 128) * -(-N // 128) >= 512:
+        t128 = -(-M // 128) * -(-N // 128)
+        if M > 64 and t128 >= 512 and 4 * t128 >= 3 * 512 * -(-t128 // 512):
             t = "128x128"
         elif -(-M // 128) * -(-N // 64) >= 2048:
             t = "128x64"

@@ -135,13 +135,14 @@ def test_every_block_size_ragged(T, dtype, ib):
 
 @pytest.mark.parametrize("schedule", ["left", "right"])
 def test_f64_updates_on_128x128_tiles(T, schedule, monkeypatch):
-    """fp64 solves whose updates are large enough for the 128 x 128 tile
-    (at least 512 tiles): right-looking m = 3000, n = 4000 at ib 256 (first
-    update 2744 x 4000, 704 tiles; the later ones fall back to smaller
-    tiles) and left-looking m = 2200, n = 8300 at ib 1024 (updates
-    1024 x 8300, 520 tiles).  Ragged last block row and column tile."""
+    """fp64 solves with updates on the 128 x 128 tile (at least 512 tiles,
+    rounds of 512 at least 3/4 full): right-looking m = 3300, n = 4000 at
+    ib 256 (first update 3044 x 4000, 768 tiles; later ones fall back to
+    smaller tiles) and left-looking m = 2200, n = 8100 at ib 1024 (first
+    update 1024 x 8100, 512 tiles; the ragged last block row of 152 rows
+    uses smaller ones).  Ragged row and column tiles."""
     monkeypatch.setenv("TRSM_SCHEDULE", schedule)
-    m, n, ib = (3000, 4000, 256) if schedule == "right" else (2200, 8300, 1024)
+    m, n, ib = (3300, 4000, 256) if schedule == "right" else (2200, 8100, 1024)
     L, B = make_problem("f64", m, n, seed=31)
     X = solve_gpu(T, L, B, 0.75, ib=ib)
     check("f64", X, oracle.solve(L, B, 0.75), f"f64 {schedule} m={m} n={n} ib={ib}")

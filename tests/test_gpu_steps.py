@@ -107,11 +107,12 @@ def test_gemm_large_tile_path(T, dtype):
 
 
 def test_gemm_fp64_128x128_tile(T):
-    """fp64 products with at least 512 tiles of 128 x 128 and 16-byte
-    aligned operands take the 128 x 128 tile: ragged M and N (2900), even K
-    with a ragged last K tile (46, 302), beta 0 and 1."""
-    gemm_case(T, "f64", 2900, 2900, 46, 1.0, -1.0, seed=5)
-    gemm_case(T, "f64", 2900, 2900, 302, 0.0, 0.5, seed=6)
+    """fp64 products whose 128 x 128 tiles fill rounds of 512 (here exactly
+    512) with 16-byte aligned operands take the 128 x 128 tile: ragged M
+    (2000) and N (4000), even K with a ragged last K tile (46, 302), beta 0
+    and 1."""
+    gemm_case(T, "f64", 2000, 4000, 46, 1.0, -1.0, seed=5)
+    gemm_case(T, "f64", 2000, 4000, 302, 0.0, 0.5, seed=6)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])

@@ -696,8 +696,12 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
         } else if constexpr (sizeof(T) == 8) {
             // (16-byte aligned operands only: the dword-load form needs
             // all 256 VGPRs and runs one wave per SIMD)
-            // (and more than 64 rows, which a 64-row tile already covers)
-            if (Mr > 64 && ((Mr + 127) / 128) * ((g.N + 127) / 128) >= 512 &&
+            // (and more than 64 rows, which a 64-row tile already covers).
+            // Its rounds of 512 tiles must also be at least 3/4 full: 585
+            // tiles (fp64 1100 x 8300) leave a second round nearly empty and
+            // ran 41.5 TFLOP/s where 64 x 64 tiles fill their rounds.
+            const int64_t t128 = ((Mr + 127) / 128) * ((g.N + 127) / 128);
+            if (Mr > 64 && t128 >= 512 && 4 * t128 >= 3 * 512 * ((t128 + 511) / 512) &&
                 aligned16(g.A, g.lda, sizeof(T)) && aligned16(g.Bm, g.ldb, sizeof(T)))
                 return launch_tile<T, 128, 128, KT>(g, st);
             if (((Mr + 127) / 128) * ((g.N + 63) / 64) >= 2048) return launch_tile<T, 128, 64, KT>(g, st);
