@@ -652,7 +652,8 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
     const dim3 grid((unsigned)(rowsM * tN), (unsigned)nz);
     const bool vec = p.a_vec && p.b_vec;
     if (g.b_lower) {
-        if constexpr (MT == 64 && NT == 32) {  // the only shape launched with it
+        // the shapes launched with it (the inversion's second product)
+        if constexpr ((MT == 64 && NT == 32) || (MT == 32 && NT == 32) || (MT == 64 && NT == 64)) {
             if (vec) hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, false, true, true>), grid, dim3(256), 0, st, p);
             else hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, false, false, true>), grid, dim3(256), 0, st, p);
         } else {
@@ -688,6 +689,16 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
 //     For fp32 and complex data it lost or spills.
 template <typename T, int KT>
 hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
+    // The batched triangular products of the diagonal inversion (split-K
+    // chunks have sKo > 0): 32 x 32 tiles for fp32, twice the workgroups of
+    // 64 x 32 for its few large pairs (fp32 4096^2: inversion 93 -> 87 us),
+    // 64 x 64 for complex fp64 (complex 8192 x 2048: 457 -> 421 us).  The
+    // tile changes no element's order of operations: the inverses are
+    // bitwise the same.
+    if (g.batch > 1 && (g.b_lower || (g.a_lower && g.sKo == 0))) {
+        if constexpr (std::is_same<T, float>::value) return launch_tile<T, 32, 32, KT>(g, st);
+        if constexpr (std::is_same<T, cplx>::value) return launch_tile<T, 64, 64, KT>(g, st);
+    }
     if (g.a_lower || g.b_lower) return launch_tile<T, 64, 32, KT>(g, st);
     if (g.batch <= 1) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
