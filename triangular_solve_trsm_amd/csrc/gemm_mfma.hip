@@ -15,7 +15,7 @@
 //
 // gfx950 mapping:
 //   * 256 threads = 2 x 2 wavefronts on a macro tile of MT x NT real rows x
-//     columns (64 x 32 up to 128 x 64 by launch shape, see launch_sized);
+//     columns (32 x 32 up to 128 x 128 by launch shape, see launch_sized);
 //     each wave owns (MT/2) x (NT/2) as 16 x 16 tiles
 //     of v_mfma_f64_16x16x4f64 (fp64, complex fp64) or
 //     v_mfma_f32_16x16x4f32 (fp32: true fp32 products, no reduced-precision
@@ -671,18 +671,18 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
 
 // Macro tile, from timings on MI355X of the update and solve sequences of
 // blocked solves (fp32 4096^2, fp64 1024^2 .. 8192^2, complex 8192 x 2048):
-//   * 64 x 32 for the triangular products (each workgroup folds two row
-//     tiles, so twice as many column tiles keep the CUs busy), for updates
-//     too small to give 1024 tiles of 64 x 64, and for batched launches (the
-//     small products of the diagonal inversion);
+//   * 64 x 32 for the triangular solve products (each workgroup folds two
+//     row tiles, so twice as many column tiles keep the CUs busy), for
+//     updates too small to give 1024 tiles of 64 x 64, and for split-K
+//     chunks; the diagonal inversion's batched products as below;
 //   * 128 x 64 (fp64) or 64 x 128 (complex, whose 64 real rows are 32
 //     complex rows) for updates that give at least 2048 such tiles: at three
 //     of these workgroups per CU, fewer leave a last round that runs the
 //     chip part empty;
 //   * 64 x 64 otherwise;
 //   * for fp64, 128 x 128 ahead of all of these once it gives at least 512
-//     tiles (two per CU, which is all its 254 VGPRs and 70 KB of LDS allow,
-//     so the first round fills the chip).  Each wave then holds 64 x 64
+//     tiles in rounds of 512 at least 3/4 full (two per CU, which is all its
+//     254 VGPRs and 70 KB of LDS allow, so the first round fills the chip).  Each wave then holds 64 x 64
 //     results, which halves the operand traffic per product against 64 x 64
 //     tiles.  Measured on the left-looking updates of fp64 8192^2 (M = 1024,
 //     N = 8192): 61.3 -> 63.4 TFLOP/s at K = 7168, the solve 9.50 -> 9.27 ms.
@@ -720,7 +720,7 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
         if (((Mr + 63) / 64) * ((g.N + 63) / 64) < 1024) return launch_tile<T, 64, 32, KT>(g, st);
         return launch_tile<T, 64, 64, KT>(g, st);
     }
-    return launch_tile<T, 64, 32, KT>(g, st);  // batched: the small products of the inversion
+    return launch_tile<T, 64, 32, KT>(g, st);  // batched: split-K chunks, other inversion products
 }
 
 // ---- split K: the reduction of the partial products -----------------------
