@@ -315,6 +315,26 @@ def test_bidiagonal_exact(T, dtype, m, ib):
     assert np.array_equal(X, np.cumsum(B, axis=0)), f"{dtype} m={m}"
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
+@pytest.mark.parametrize("m,n,ib", [(40, 20, 0), (300, 50, 128), (1100, 70, 512)])
+def test_zero_pivot_propagates_non_finite(T, dtype, m, n, ib):
+    """No singularity check (BLAS convention): with l_kk = 0 the solve
+    still completes; rows above k depend only on the leading k x k block and
+    match the oracle, and every row from k down is non-finite, as in the
+    oracle.  Direct path (m <= 64) and blocked path with the zero pivot
+    inside a diagonal block."""
+    k = m // 2 + 3
+    L, B = make_problem(dtype, m, n, seed=77 + m)
+    L = L.copy(order="F")
+    L[k, k] = 0
+    X = solve_gpu(T, L, B, 1.0, ib=ib) if ib else solve_gpu(T, L, B, 1.0)
+    ref = oracle.solve(L, B, 1.0)
+    assert np.all(~np.isfinite(ref[k:])), "oracle: rows from the zero pivot down are non-finite"
+    assert np.all(np.isfinite(X[:k])), f"{dtype} m={m}: rows above the zero pivot must stay finite"
+    check(dtype, X[:k], ref[:k], f"{dtype} m={m} rows above the zero pivot")
+    assert np.all(~np.isfinite(X[k:])), f"{dtype} m={m}: rows from the zero pivot down must be non-finite"
+
+
 @pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
 def test_deterministic(T, dtype):
     L, B = make_problem(dtype, 900, 300, seed=5)

@@ -155,15 +155,24 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
             const int r = u % R;
             if (k >= j0 && k < bs) {  // wave-uniform
                 const int kb = k / R;  // lane owning row k
+                // Column j of the inverse is solved from step j on; before
+                // that its row k is zero, and its solved value is zero too
+                // (not 0 * (1/d_kk), which is NaN when d_kk is 0: such a NaN
+                // would land above the diagonal, where W must hold zeros).
                 T s[P];
 #pragma unroll
-                for (int jj = 0; jj < P; ++jj) s[jj] = bcast(E::mul(x[r][jj], inv[r]), kb);
-                // rows below the pivot: x_i -= d_ik s (d masked to 0 for i <= k)
+                for (int jj = 0; jj < P; ++jj)
+                    s[jj] = bcast(E::sel(j0 + jj <= k, E::mul(x[r][jj], inv[r]), E::zero()), kb);
+                // rows below the pivot: x_i -= d_ik s.  Rows i <= k are left
+                // as they are by a select (a zero d would still turn an
+                // infinite s into NaN there).
 #pragma unroll
                 for (int rr = 0; rr < R; ++rr) {
-                    const T d = E::sel(row0 + rr > k, ring[slot][rr], E::zero());
+                    const bool below = row0 + rr > k;
+                    const T d = ring[slot][rr];
 #pragma unroll
-                    for (int jj = 0; jj < P; ++jj) x[rr][jj] = E::msub(x[rr][jj], d, s[jj]);
+                    for (int jj = 0; jj < P; ++jj)
+                        x[rr][jj] = E::sel(below, E::msub(x[rr][jj], d, s[jj]), x[rr][jj]);
                 }
                 // the pivot row itself takes the solved values
                 const bool own = lane == kb;
