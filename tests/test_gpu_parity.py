@@ -335,6 +335,35 @@ def test_zero_pivot_propagates_non_finite(T, dtype, m, n, ib):
     assert np.all(~np.isfinite(X[k:])), f"{dtype} m={m}: rows from the zero pivot down must be non-finite"
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
+@pytest.mark.parametrize("m,n,ib", [(40, 20, 0), (300, 40, 128), (1100, 30, 512)])
+def test_non_finite_b_entry_stays_in_its_column(T, dtype, m, n, ib):
+    """A NaN in B at (k, j): every other column matches the oracle; in
+    column j the rows of earlier diagonal blocks match the oracle and every
+    row from k down is non-finite.  The rows between the start of k's block
+    and k may also turn NaN (the method multiplies the block by its inverse,
+    whose zeros above the diagonal meet the NaN); those that stay finite
+    match the oracle.  Block: the 16-row panel on the direct path, ib rows
+    on the blocked path."""
+    k, j = m // 2 + 5, n // 3
+    L, B = make_problem(dtype, m, n, seed=91 + m)
+    B = B.copy(order="F")
+    B[k, j] = np.nan
+    X = solve_gpu(T, L, B, 1.0, ib=ib) if ib else solve_gpu(T, L, B, 1.0)
+    ref = oracle.solve(L, B, 1.0)
+    others = [c for c in range(n) if c != j]
+    check(dtype, X[:, others], ref[:, others], f"{dtype} m={m}: columns without the NaN")
+    start = (k // (ib if ib else 16)) * (ib if ib else 16)
+    col, rcol = X[:, j], ref[:, j]
+    assert np.all(np.isfinite(col[:start])), f"{dtype} m={m}: rows of earlier blocks must stay finite"
+    if start:
+        check(dtype, col[:start], rcol[:start], f"{dtype} m={m}: column {j} above the NaN's block")
+    assert np.all(~np.isfinite(col[k:])), f"{dtype} m={m}: rows from the NaN down must be non-finite"
+    fin = np.isfinite(col[start:k])
+    if fin.any():
+        check(dtype, col[start:k][fin], rcol[start:k][fin], f"{dtype} m={m}: finite rows of the NaN's block")
+
+
 @pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
 def test_deterministic(T, dtype):
     L, B = make_problem(dtype, 900, 300, seed=5)
