@@ -120,16 +120,19 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
     const int np = (m + 15) >> 4;  // panels that hold rows < m
 
     // ---- 1. this wave's 16 columns, all rows, into accumulators ----------
-    // Issued first: B does not depend on L, so these loads are in flight
-    // while L is staged and inverted (measured faster than loading B after
-    // the inversion, although the longer register life leaves three waves
-    // per SIMD for complex instead of four).
+    // B does not depend on L, so its loads are in flight while L is staged
+    // and inverted (measured faster than loading B after the inversion,
+    // although the longer register life leaves three waves per SIMD for
+    // complex instead of four).  With buffer loads they are issued right
+    // after L's: loads complete in order, so waiting for L then leaves B in
+    // flight, and panel p of the solve below waits only for its own rows.
     const int64_t col = cgi * 64 + w * 16 + c;
     const bool colok = col < n;
     T *__restrict__ Bc = Bp + col * ldb;
     const __amdgpu_buffer_rsrc_t rsb =
         make_rsrc(Bp, BUF ? ((n - 1) * ldb + m) * (int64_t)sizeof(T) : 0);
     d4 acc[kPanels][TILES];
+    auto load_b = [&]() {
 #pragma unroll
     for (int p = 0; p < kPanels; ++p) {
 #pragma unroll
@@ -161,6 +164,9 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
         }
     }
 
+    };
+    if constexpr (!BUF) load_b();
+
     // ---- 2. lower blocks of L into LDS (rows >= m: identity) ---------------
     {
         const int i = tid & 15, k = tid >> 4;
@@ -176,6 +182,7 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
                     const int gi = 16 * q + i, gk = 16 * p + k;
                     v[blk(q, p)] = ld_elem<T>(rs, gi + (int64_t)gk * lda, gi < m && gk < m && gi >= gk);
                 }
+            load_b();  // B's loads behind L's (see phase 1)
 #pragma unroll
             for (int q = 0; q < kPanels; ++q)
 #pragma unroll
@@ -225,11 +232,26 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
     }
     __syncthreads();
 
-    // ---- 4. X_p = W_p B_p, B_q -= L_qp X_p --------------------------------
+    // ---- 4. B_p -= sum_{q<p} L_pq X_q, then X_p = W_p B_p ------------------
+    // Panel p takes the updates of the panels above it just before its own
+    // product (the same updates in the same order as updating every panel
+    // below as soon as a panel is solved), so the products of panel p need
+    // only B_p and the solved panels: the rows of later panels may still be
+    // arriving.
     const T alpha = E::from(alpha_s);
 #pragma unroll
     for (int p = 0; p < kPanels; ++p) {
         if (p < np) {  // uniform
+#pragma unroll
+        for (int q = 0; q < p; ++q)
+#pragma unroll
+            for (int a = 0; a < TILES; ++a)
+#pragma unroll
+                for (int t = 0; t < TILES; ++t)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+                        acc[p][a] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                            afrag(Lb[blk(p, q)], a, t, s, c, g, -1.0), acc[q][t][s], acc[p][a], 0, 0, 0);
         d4 x[TILES];
 #pragma unroll
         for (int a = 0; a < TILES; ++a) {
@@ -245,20 +267,6 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
         // so no panel's products wait for another panel's stores to drain
 #pragma unroll
         for (int a = 0; a < TILES; ++a) acc[p][a] = x[a];
-        // update the panels below
-#pragma unroll
-        for (int q = p + 1; q < kPanels; ++q) {
-            if (q < np) {  // uniform
-#pragma unroll
-            for (int a = 0; a < TILES; ++a)
-#pragma unroll
-                for (int t = 0; t < TILES; ++t)
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-                        acc[q][a] = __builtin_amdgcn_mfma_f64_16x16x4f64(
-                            afrag(Lb[blk(q, p)], a, t, s, c, g, -1.0), x[t][s], acc[q][a], 0, 0, 0);
-            }
-        }
         }
     }
 
