@@ -159,20 +159,28 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
                 // that its row k is zero, and its solved value is zero too
                 // (not 0 * (1/d_kk), which is NaN when d_kk is 0: such a NaN
                 // would land above the diagonal, where W must hold zeros).
+                // Only the task's first P - 1 steps have columns that are not
+                // yet active (a uniform test).
                 T s[P];
+                if (k >= j0 + P - 1) {
 #pragma unroll
-                for (int jj = 0; jj < P; ++jj)
-                    s[jj] = bcast(E::sel(j0 + jj <= k, E::mul(x[r][jj], inv[r]), E::zero()), kb);
-                // rows below the pivot: x_i -= d_ik s.  Rows i <= k are left
-                // as they are by a select (a zero d would still turn an
-                // infinite s into NaN there).
-#pragma unroll
-                for (int rr = 0; rr < R; ++rr) {
-                    const bool below = row0 + rr > k;
-                    const T d = ring[slot][rr];
+                    for (int jj = 0; jj < P; ++jj) s[jj] = bcast(E::mul(x[r][jj], inv[r]), kb);
+                } else {
 #pragma unroll
                     for (int jj = 0; jj < P; ++jj)
-                        x[rr][jj] = E::sel(below, E::msub(x[rr][jj], d, s[jj]), x[rr][jj]);
+                        s[jj] = bcast(E::sel(j0 + jj <= k, E::mul(x[r][jj], inv[r]), E::zero()), kb);
+                }
+                // rows below the pivot: x_i -= d_ik s.  Rows i <= k are left
+                // as they are (a zero d would still turn an infinite s into
+                // NaN there); the condition is per lane, so the update is
+                // masked rather than selected element by element.
+#pragma unroll
+                for (int rr = 0; rr < R; ++rr) {
+                    if (row0 + rr > k) {
+                        const T d = ring[slot][rr];
+#pragma unroll
+                        for (int jj = 0; jj < P; ++jj) x[rr][jj] = E::msub(x[rr][jj], d, s[jj]);
+                    }
                 }
                 // the pivot row itself takes the solved values
                 const bool own = lane == kb;
