@@ -115,6 +115,15 @@ def test_gemm_fp64_128x128_tile(T):
     gemm_case(T, "f64", 2000, 4000, 302, 0.0, 0.5, seed=6)
 
 
+@pytest.mark.parametrize("dtype", ["f64", "c64"])
+def test_gemm_triangular_wide_tiles(T, dtype):
+    """Triangular products with 512 folded workgroups on the wider tile
+    (fp64 64 x 128, complex 64 x 64): ragged M (1000 rows, the last row tile
+    short) and ragged N."""
+    N = 8100 if dtype == "f64" else 2000
+    gemm_case(T, dtype, 1000, N, 1000, 0.0, 0.5 if dtype == "f64" else 0.5 - 0.25j, seed=12, a_lower=True)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_gemm_split_routing(T, dtype):
     for split in (16, 37, 100):
