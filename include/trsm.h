@@ -33,8 +33,12 @@
  * inverted diagonal blocks, one panel of B and, when B is narrow, the
  * partial sums of products split along K (at most 2^21 elements).  The
  * library allocates it per (device, stream), grows it on demand and keeps
- * it until trsm_release_workspace().  Calls on the same stream are ordered and share
- * it safely; concurrent calls on different streams each get their own.
+ * it until trsm_release_workspace().  Calls on the same stream share it:
+ * a call holds the stream's workspace from the moment it takes it until
+ * it has enqueued its last kernel, so calls from several host threads on
+ * one stream are serialised while they enqueue (growth waits for the
+ * stream before freeing the old buffer); calls on different streams each
+ * get their own workspace and run concurrently.
  */
 #ifndef TRSM_MI355X_H
 #define TRSM_MI355X_H
@@ -71,6 +75,9 @@ typedef enum trsm_dtype_t {
  *          float[2] (re, im), by dtype.
  *   A      device pointer, m x m, lda >= max(1, m).
  *   B      device pointer, m x n, ldb >= max(1, m); overwritten with X.
+ *   Every leading dimension the rules above allow is supported, however
+ *   large (a sub-block of a tall array): tiles whose columns span more than
+ *   a 32-bit offset reaches are read through 64-bit addresses.
  * Quick returns: m == 0 or n == 0 does nothing; alpha == 0 sets B = 0
  * without reading A.  A, B and alpha may be NULL only when m*n == 0.
  * Regime (section 4.1 of the pages): m <= 64 runs the single-workgroup

@@ -108,7 +108,7 @@ def test_python_binding_rejects_bad_layouts(T):
     import torch
     A = torch.zeros(4, 4, dtype=torch.float64)
     B = torch.zeros(4, 3, dtype=torch.float64)       # row-major: stride(0) != 1
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="column-major"):
         T.trsm_lln(A.T, B, 1.0)
     with pytest.raises(TypeError):
         T.trsm_lln(A.T, torch.zeros(3, 4, dtype=torch.int32).T, 1.0)
@@ -194,3 +194,21 @@ def test_block_size_lookup_matches_table(T):
             best = min(dist(e) for e in entries)
             allowed = {e[2] for e in entries if abs(dist(e) - best) < 1e-9}  # ties: any of them
             assert T.trsm_lln_select_ib(dt, m, n) in allowed, (dt, m, n)
+
+
+def test_python_binding_rejects_host_tensors(T):
+    """Host (CPU) tensors never reach the library: their pointers would be
+    taken as device addresses by the kernels.  Every binding raises before
+    it calls into the library (no GPU is needed, and none is touched)."""
+    import torch
+    A = torch.zeros(70, 70, dtype=torch.float64).T
+    B = torch.zeros(3, 70, dtype=torch.float64).T
+    for call_ in (lambda: T.trsm_lln(A, B, 1.0),
+                  lambda: T.trsm_lln_ex(A, B, 1.0, ib=64),
+                  lambda: T.trsm_solve(A, B, 1.0, side="L", uplo="U", trans="T"),
+                  lambda: T.trsm_lln_strided_batched(A.unsqueeze(0), B.unsqueeze(0), 1.0),
+                  lambda: T.trsm_kernel_diag_inv(A, torch.zeros(2 * 64 * 64, dtype=torch.float64), 64),
+                  lambda: T.trsm_kernel_gemm(A, B, torch.zeros(3, 70, dtype=torch.float64).T[:70])):
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call_()
+

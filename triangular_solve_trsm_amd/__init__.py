@@ -136,6 +136,31 @@ def _ld(t, rows: int, cols: int) -> int:
     return max(ld, 1)
 
 
+def _check_device(where: str, *tensors, stream=None):
+    """Every operand must be a tensor in GPU memory, all on one device, and
+    an explicit torch stream must belong to that device: the library takes
+    raw device pointers, and a host pointer reaching a kernel faults the GPU.
+    Raises before anything is handed to the library."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not getattr(t, "is_cuda", False):
+            raise ValueError(f"{where}: every operand must be a GPU tensor (got one on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{where}: operands on different devices ({dev} and {t.device})")
+    sdev = getattr(stream, "device", None)
+    if dev is not None and sdev is not None and sdev != dev:
+        raise ValueError(f"{where}: stream on {sdev} but operands on {dev}")
+    if dev is not None:
+        import torch
+        if torch.cuda.current_device() != dev.index:
+            raise ValueError(f"{where}: operands on {dev} but the current device is "
+                             f"cuda:{torch.cuda.current_device()} (use torch.cuda.device)")
+
+
 def _check(status: int, where: str):
     if status != 0:
         raise TrsmError(status, where)
@@ -160,9 +185,11 @@ def trsm_lln(A, B, alpha=1.0, *, stream=None):
     m, n = B.shape
     if tuple(A.shape) != (m, m):
         raise ValueError(f"A must be {m} x {m}")
+    lda, ldb = _ld(A, m, m), _ld(B, m, n)
+    _check_device("trsm_lln", A, B, stream=stream)
     al = alpha_buffer(code, alpha)
-    st = lib.trsm_lln(code, m, n, ctypes.addressof(al), A.data_ptr(), _ld(A, m, m),
-                      B.data_ptr(), _ld(B, m, n), _stream_handle(stream))
+    st = lib.trsm_lln(code, m, n, ctypes.addressof(al), A.data_ptr(), lda, B.data_ptr(), ldb,
+                      _stream_handle(stream))
     _check(st, "trsm_lln")
     return B
 
@@ -181,9 +208,11 @@ def trsm_solve(A, B, alpha=1.0, *, side="L", uplo="L", trans="N", diag="N", stre
         raise ValueError(f"A must be {k} x {k}")
     flags = ({"L": 0, "R": 1}[side], {"L": 0, "U": 1}[uplo], {"N": 0, "T": 1, "C": 2}[trans],
              {"N": 0, "U": 1}[diag])
+    lda, ldb = _ld(A, k, k), _ld(B, m, n)
+    _check_device("trsm_solve", A, B, stream=stream)
     al = alpha_buffer(code, alpha)
-    st = lib.trsm_solve(*flags, code, m, n, ctypes.addressof(al), A.data_ptr(), _ld(A, k, k),
-                        B.data_ptr(), _ld(B, m, n), _stream_handle(stream))
+    st = lib.trsm_solve(*flags, code, m, n, ctypes.addressof(al), A.data_ptr(), lda,
+                        B.data_ptr(), ldb, _stream_handle(stream))
     _check(st, "trsm_solve")
     return B
 
@@ -197,10 +226,11 @@ def trsm_lln_ex(A, B, alpha=1.0, ib: int = 0, force_blocked: bool = False, *, st
     m, n = B.shape
     if tuple(A.shape) != (m, m):
         raise ValueError(f"A must be {m} x {m}")
+    lda, ldb = _ld(A, m, m), _ld(B, m, n)
+    _check_device("trsm_lln_ex", A, B, stream=stream)
     al = alpha_buffer(code, alpha)
-    st = lib.trsm_lln_ex(code, m, n, ctypes.addressof(al), A.data_ptr(), _ld(A, m, m),
-                         B.data_ptr(), _ld(B, m, n), int(ib), int(bool(force_blocked)),
-                         _stream_handle(stream))
+    st = lib.trsm_lln_ex(code, m, n, ctypes.addressof(al), A.data_ptr(), lda, B.data_ptr(), ldb,
+                         int(ib), int(bool(force_blocked)), _stream_handle(stream))
     _check(st, "trsm_lln_ex")
     return B
 
@@ -214,11 +244,12 @@ def trsm_lln_strided_batched(A, B, alpha=1.0, *, stream=None):
     batch, m, n = B.shape
     if tuple(A.shape) != (batch, m, m):
         raise ValueError(f"A must be {batch} x {m} x {m}")
+    lda, ldb = _ld(A, m, m), _ld(B, m, n)
+    _check_device("trsm_lln_strided_batched", A, B, stream=stream)
     al = alpha_buffer(code, alpha)
-    st = lib.trsm_lln_strided_batched(code, m, n, ctypes.addressof(al), A.data_ptr(),
-                                      _ld(A, m, m), A.stride(0) if batch > 1 else 0,
-                                      B.data_ptr(), _ld(B, m, n), B.stride(0) if batch > 1 else 0,
-                                      batch, _stream_handle(stream))
+    st = lib.trsm_lln_strided_batched(code, m, n, ctypes.addressof(al), A.data_ptr(), lda,
+                                      A.stride(0) if batch > 1 else 0, B.data_ptr(), ldb,
+                                      B.stride(0) if batch > 1 else 0, batch, _stream_handle(stream))
     _check(st, "trsm_lln_strided_batched")
     return B
 
@@ -251,6 +282,7 @@ def trsm_kernel_diag_inv(A, W, ib: int, *, stream=None):
     nb = (m + ib - 1) // ib
     if W.dtype != A.dtype or W.numel() < nb * ib * ib or not W.is_contiguous():
         raise ValueError("W must be a contiguous buffer of ceil(m/ib)*ib*ib elements of A's dtype")
+    _check_device("trsm_kernel_diag_inv", A, W, stream=stream)
     st = lib.trsm_kernel_diag_inv(code, int(ib), m, A.data_ptr(), _ld(A, m, m), W.data_ptr(),
                                   _stream_handle(stream))
     _check(st, "trsm_kernel_diag_inv")
@@ -266,6 +298,7 @@ def trsm_kernel_gemm(A, Bm, D, *, beta=0.0, gamma=1.0, C=None, D2=None, split: i
     K2, N = Bm.shape
     if K2 != K or tuple(D.shape) != (M, N):
         raise ValueError("shape mismatch")
+    _check_device("trsm_kernel_gemm", A, Bm, D, C, D2, stream=stream)
     b = alpha_buffer(code, beta)
     g = alpha_buffer(code, gamma)
     c_ptr = C.data_ptr() if C is not None else None

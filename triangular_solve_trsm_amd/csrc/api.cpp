@@ -4,20 +4,24 @@
 // Dispatch follows the hierarchical framework of HSMA-TRSM ("Hierarchical
 // Shared Memory-Aware Optimization for TRSM on GPU Platforms", section 4.1,
 // Figure 2): m <= 64 takes the direct solve (kernel a); larger m takes the
-// blocked algorithm of section 4.3 with the block size from the offline
-// table of section 4.3.2.
+// blocked algorithm of section 4.3 with the block size, and the order of
+// phase 2, from the offline table of section 4.3.2.
 //
-// Blocked driver (section 4.3, right-looking form of phase 2):
-//   phase 1:  W_t = D_t^{-1} for every diagonal block, one launch;
+// Blocked driver (section 4.3):
+//   phase 1:  W_t = D_t^{-1} for every diagonal block (diag_inv_launch);
 //   copy B_0 -> P (panel buffer, ld = ib);
 //   for r = 0 .. nb-1:
 //     solve:   B_r = g_r * W_r * P          (g_0 = alpha, else 1; triangular W)
-//     update:  rows below block r:  beta_r * B_{r+1:} - L_{r+1:, r} * B_r,
-//              with beta_0 = alpha, else 1; the rows of block r+1 are written
-//              to P (the next solve's input), the rest in place.
-// The pages state the update left-looking (B_r -= A_{r,[0:r]} X_{[0:r]});
-// the right-looking order computes the same sums with one GEMM of K = ib per
-// block row, whose M x N extent keeps all 256 CUs busy early on.
+//     then the next block row's right-hand side goes to P, in one of two
+//     orders that form the same sums:
+//     left-looking (the pages' order, "Phase 2"): one GEMM for block row
+//              r+1 alone,  P = alpha B_{r+1} - L_{r+1, 0:r+1} X_{0:r+1},
+//              K = (r+1) ib;
+//     right-looking: every row below block r at once,
+//              B_{r+1:} = beta_r B_{r+1:} - L_{r+1:, r} X_r  (beta_0 = alpha,
+//              else 1), K = ib, with the rows of block r+1 routed to P.
+// The table records which order measured faster for each (type, m, n);
+// products with few output tiles are split along K (gemm_splitk_launch).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -26,6 +30,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <tuple>
 #include <utility>
@@ -65,8 +70,28 @@ struct DevInfo {
 std::map<int, DevInfo> g_dev;                                  // device -> properties
 // Workspace per (device, stream, slot): slot 0 serves the solve (inverses,
 // panel), slot 1 the staging copies of the general variants, which stay in
-// use while the solve runs.
-std::map<std::tuple<int, hipStream_t, int>, std::pair<void *, size_t>> g_ws;
+// use while the solve runs.  A call holds its slot's mutex from the moment
+// it takes the buffer until it has enqueued its last kernel (WsLease), so a
+// second host thread on the same stream can neither free nor replace the
+// buffer while the first still has launches to enqueue that use it.  Slots
+// are created under g_mu and never destroyed, so their addresses stay valid.
+struct WsSlot {
+    std::mutex mu;
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::map<std::tuple<int, hipStream_t, int>, std::unique_ptr<WsSlot>> g_ws;
+
+class WsLease {
+  public:
+    WsLease() = default;
+    WsLease(const WsLease &) = delete;
+    WsLease &operator=(const WsLease &) = delete;
+    void hold(std::mutex &mu) { lk_ = std::unique_lock<std::mutex>(mu); }
+
+  private:
+    std::unique_lock<std::mutex> lk_;
+};
 
 trsm_status_t check_device(int *dev_out, int *cus_out = nullptr) {
     int dev = 0;
@@ -84,15 +109,26 @@ trsm_status_t check_device(int *dev_out, int *cus_out = nullptr) {
     return it->second.ok ? TRSM_STATUS_SUCCESS : TRSM_STATUS_NOT_SUPPORTED;
 }
 
-trsm_status_t get_workspace(int dev, hipStream_t st, size_t bytes, void **out, int slot = 0) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    auto &e = g_ws[std::make_tuple(dev, st, slot)];
-    if (e.second < bytes) {
-        if (e.first) {
+// Takes the workspace of (dev, st, slot), at least `bytes` long, and holds
+// it in `lease` until the lease is destroyed.  Growing it waits for the
+// stream (every earlier call's kernels that use the old buffer have been
+// enqueued before this one got the lease) and frees the old buffer.
+trsm_status_t get_workspace(int dev, hipStream_t st, size_t bytes, void **out, WsLease &lease,
+                            int slot = 0) {
+    WsSlot *w = nullptr;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto &e = g_ws[std::make_tuple(dev, st, slot)];
+        if (!e) e.reset(new WsSlot);
+        w = e.get();
+    }
+    lease.hold(w->mu);
+    if (w->bytes < bytes) {
+        if (w->ptr) {
             if (hipStreamSynchronize(st) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
-            (void)hipFree(e.first);
-            e.first = nullptr;
-            e.second = 0;
+            (void)hipFree(w->ptr);
+            w->ptr = nullptr;
+            w->bytes = 0;
         }
         const char *fail = std::getenv("TRSM_FAIL_ALLOC");  // test hook
         if (fail && fail[0] == '1') return TRSM_STATUS_ALLOC_FAILED;
@@ -101,10 +137,10 @@ trsm_status_t get_workspace(int dev, hipStream_t st, size_t bytes, void **out, i
             (void)hipGetLastError();
             return TRSM_STATUS_ALLOC_FAILED;
         }
-        e.first = p;
-        e.second = bytes;
+        w->ptr = p;
+        w->bytes = bytes;
     }
-    *out = e.first;
+    *out = w->ptr;
     return TRSM_STATUS_SUCCESS;
 }
 
@@ -247,45 +283,67 @@ int64_t splitk_target() {
     return kSplitKTarget;
 }
 
-// Blocked path for one problem (m > 0, n > 0, alpha != 0).
-trsm_status_t run_blocked(int dt, int64_t m, int64_t n, Scalar alpha, const void *A,
-                          int64_t lda, void *B, int64_t ldb, int ib, bool table_left, int dev,
-                          hipStream_t st) {
-    const bool left = use_left_looking(table_left);
+// Host-side plan of the blocked path for one problem: block size, phase-2
+// order, the split-K factor of every product and the workspace it needs
+// (inverses W, panel P, split-K partial sums).  Makes no HIP call.
+struct BlockedPlan {
+    int ib = 0;
+    bool left = false;
+    int64_t nb = 0;
+    size_t wbytes = 0, pbytes = 0, partbytes = 0;
+    std::vector<int> solve_parts, update_parts;
+    size_t bytes() const { return wbytes + pbytes + partbytes; }
+};
+
+BlockedPlan plan_blocked(int dt, int64_t m, int64_t n, int ib, bool table_left) {
+    BlockedPlan pl;
+    pl.ib = ib;
+    pl.left = use_left_looking(table_left);
     const size_t es = dtype_size(dt);
-    const int64_t nb = (m + ib - 1) / ib;
-    size_t wbytes = (size_t)nb * ib * ib * es;
-    wbytes = (wbytes + 255) & ~(size_t)255;
+    pl.nb = (m + ib - 1) / ib;
+    pl.wbytes = ((size_t)pl.nb * ib * ib * es + 255) & ~(size_t)255;
     // the panel buffer P doubles as the inversion's scratch (P is first
     // written after the inversion, in the same stream)
     size_t pbytes = (size_t)ib * n * es;
     const size_t tbytes = (size_t)diag_inv_tmp_elems(ib, m) * es;
     if (tbytes > pbytes) pbytes = tbytes;
-    pbytes = (pbytes + 255) & ~(size_t)255;
+    pl.pbytes = (pbytes + 255) & ~(size_t)255;
     // split-K factor of every phase-2 product, and the partial sums they need
     const int64_t target = splitk_target();
-    std::vector<int> solve_parts((size_t)nb, 1), update_parts((size_t)nb, 1);
+    pl.solve_parts.assign((size_t)pl.nb, 1);
+    pl.update_parts.assign((size_t)pl.nb, 1);
     int64_t part_elems = 0;
-    for (int64_t r = 0; r < nb; ++r) {
+    for (int64_t r = 0; r < pl.nb; ++r) {
         const int64_t r0 = r * ib;
         const int64_t bs = (m - r0) < ib ? (m - r0) : ib;
         int p = gemm_splitk_parts(dt, bs, n, bs, target);
-        solve_parts[(size_t)r] = p;
+        pl.solve_parts[(size_t)r] = p;
         if (p > 1) part_elems = std::max(part_elems, p * bs * n);
-        if (r + 1 == nb) break;
+        if (r + 1 == pl.nb) break;
         const int64_t mrest = m - r0 - bs;
         const int64_t bsn = mrest < ib ? mrest : ib;
-        p = left ? gemm_splitk_parts(dt, bsn, n, r0 + bs, target)
-                 : gemm_splitk_parts(dt, mrest, n, bs, target);
-        update_parts[(size_t)r] = p;
-        if (p > 1) part_elems = std::max(part_elems, p * (left ? bsn : mrest) * n);
+        p = pl.left ? gemm_splitk_parts(dt, bsn, n, r0 + bs, target)
+                    : gemm_splitk_parts(dt, mrest, n, bs, target);
+        pl.update_parts[(size_t)r] = p;
+        if (p > 1) part_elems = std::max(part_elems, p * (pl.left ? bsn : mrest) * n);
     }
-    void *ws = nullptr;
-    trsm_status_t s = get_workspace(dev, st, wbytes + pbytes + (size_t)part_elems * es, &ws);
-    if (s != TRSM_STATUS_SUCCESS) return s;
+    pl.partbytes = (size_t)part_elems * es;
+    return pl;
+}
+
+// Blocked path for one problem (m > 0, n > 0, alpha != 0), on the workspace
+// `ws` of at least pl.bytes() bytes.
+trsm_status_t exec_blocked(const BlockedPlan &pl, int dt, int64_t m, int64_t n, Scalar alpha,
+                           const void *A, int64_t lda, void *B, int64_t ldb, void *ws,
+                           hipStream_t st) {
+    const bool left = pl.left;
+    const int ib = pl.ib;
+    const int64_t nb = pl.nb;
+    const size_t es = dtype_size(dt);
+    const std::vector<int> &solve_parts = pl.solve_parts, &update_parts = pl.update_parts;
     char *W = static_cast<char *>(ws);
-    void *P = W + wbytes;
-    void *Part = part_elems > 0 ? W + wbytes + pbytes : nullptr;
+    void *P = W + pl.wbytes;
+    void *Part = pl.partbytes > 0 ? W + pl.wbytes + pl.pbytes : nullptr;
     const char *Ab = static_cast<const char *>(A);
     char *Bb = static_cast<char *>(B);
     if (log_enabled())
@@ -409,12 +467,15 @@ trsm_status_t run(int dt, int64_t m, int64_t n, const void *alpha_p, const void 
         return hip_status(small_lln_launch(dt, (int)m, n, alpha, A, lda, sA, B, ldb, sB, batch, st));
     }
     const IbEntry cfg = select_entry(dt, m, n);
-    const int ib = ib_forced ? ib_forced : cfg.ib;
+    const BlockedPlan pl = plan_blocked(dt, m, n, ib_forced ? ib_forced : cfg.ib, cfg.left != 0);
     const size_t es = dtype_size(dt);
+    void *ws = nullptr;
+    WsLease lease;  // held until every launch below is enqueued
+    s = get_workspace(dev, st, pl.bytes(), &ws, lease);
+    if (s != TRSM_STATUS_SUCCESS) return s;
     for (int64_t p = 0; p < batch; ++p) {
-        s = run_blocked(dt, m, n, alpha, static_cast<const char *>(A) + (size_t)(p * sA) * es, lda,
-                        static_cast<char *>(B) + (size_t)(p * sB) * es, ldb, ib, cfg.left != 0,
-                        dev, st);
+        s = exec_blocked(pl, dt, m, n, alpha, static_cast<const char *>(A) + (size_t)(p * sA) * es,
+                         lda, static_cast<char *>(B) + (size_t)(p * sB) * es, ldb, ws, st);
         if (s != TRSM_STATUS_SUCCESS) return s;
     }
     return TRSM_STATUS_SUCCESS;
@@ -491,7 +552,8 @@ trsm_status_t trsm_solve(trsm_side_t side, trsm_fill_t uplo, trsm_op_t trans, tr
         const size_t abytes = ((size_t)k * (size_t)k * es + 255) & ~(size_t)255;
         const size_t bbytes = b_in_place ? 0 : (size_t)k * (size_t)nrhs * es;
         void *ws = nullptr;
-        s = get_workspace(dev, stream, abytes + bbytes, &ws, 1);
+        WsLease lease;  // the staging slot, held until the copy back is enqueued
+        s = get_workspace(dev, stream, abytes + bbytes, &ws, lease, 1);
         if (s != TRSM_STATUS_SUCCESS) return s;
         void *Ap = ws;
         void *Bp = static_cast<char *>(ws) + abytes;
@@ -549,9 +611,10 @@ trsm_status_t trsm_kernel_diag_inv(trsm_dtype_t dtype, int ib, int64_t m, const 
         trsm_status_t s = check_device(&dev);
         if (s != TRSM_STATUS_SUCCESS) return s;
         void *tmp = nullptr;
+        WsLease lease;
         const size_t tbytes = (size_t)diag_inv_tmp_elems(ib, m) * dtype_size(dtype);
         if (tbytes > 0) {
-            s = get_workspace(dev, stream, tbytes, &tmp);
+            s = get_workspace(dev, stream, tbytes, &tmp, lease);
             if (s != TRSM_STATUS_SUCCESS) return s;
         }
         LaunchTimer t(TRSM_KERNEL_DIAG_INV, dtype, m, ib, 0, (m + ib - 1) / ib, stream);
@@ -674,17 +737,26 @@ const char *trsm_status_string(trsm_status_t status) {
 
 trsm_status_t trsm_release_workspace(void) {
     try {
-        std::lock_guard<std::mutex> lk(g_mu);
+        // Slots are taken one at a time (never two locks together), and
+        // g_mu is not held while waiting for a slot: a call holding a slot
+        // may still need g_mu or a second slot.
+        std::vector<std::pair<int, WsSlot *>> slots;
+        {
+            std::lock_guard<std::mutex> lk(g_mu);
+            for (auto &kv : g_ws) slots.emplace_back(std::get<0>(kv.first), kv.second.get());
+        }
         trsm_status_t s = TRSM_STATUS_SUCCESS;
         int cur = 0;
         const bool have_cur = hipGetDevice(&cur) == hipSuccess;
-        for (auto &kv : g_ws) {
-            if (!kv.second.first) continue;
-            if (hipSetDevice(std::get<0>(kv.first)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        for (auto &ds : slots) {
+            std::lock_guard<std::mutex> lk(ds.second->mu);
+            if (!ds.second->ptr) continue;
+            if (hipSetDevice(ds.first) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
                 s = TRSM_STATUS_HIP_ERROR;
-            (void)hipFree(kv.second.first);
+            (void)hipFree(ds.second->ptr);
+            ds.second->ptr = nullptr;
+            ds.second->bytes = 0;
         }
-        g_ws.clear();
         if (have_cur) (void)hipSetDevice(cur);
         return s;
     } catch (...) {

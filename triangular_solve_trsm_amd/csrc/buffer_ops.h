@@ -42,6 +42,21 @@ __device__ __forceinline__ u4v ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     }
 }
 
+// 16 bytes at byte offset `off` from `base` through 64-bit global
+// addresses, for operands whose leading dimension puts a tile's offsets past
+// what a 32-bit buffer offset reaches.  Each dword is read only when it lies
+// inside [0, lim) bytes from base, and is zero otherwise (no memory access),
+// which is the same contract as a raw buffer load with range lim.
+__device__ __forceinline__ u4v ld16_wide(const char *base, int64_t off, int64_t lim) {
+    u4v v;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int64_t o = off + 4 * d;
+        v[d] = (o + 4 <= lim) ? *reinterpret_cast<const unsigned *>(base + o) : 0u;
+    }
+    return v;
+}
+
 // N consecutive elements of T at byte offset `off` into dst, as 16-byte
 // loads where N * sizeof(T) allows it and dword loads otherwise.
 template <typename T, int N, bool VEC>

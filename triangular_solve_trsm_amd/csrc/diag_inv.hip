@@ -83,7 +83,11 @@ constexpr int ring_cols() {
 // [t*64R, ..)) is written at its place inside the ldw x ldw blocks of W
 // (ldw a multiple of 64R): parent block t*64R / ldw, at rows and columns
 // (t*64R) % ldw of it.
-template <typename T, int R, int P, bool VEC>
+// WIDE: lda is so large that the 64R columns of one diagonal block span
+// more than a 32-bit buffer offset reaches; each column of D then gets a
+// buffer resource of its own (its base is wave-uniform, so this is scalar
+// work), and the pivots are read with 64-bit addresses.
+template <typename T, int R, int P, bool VEC, bool WIDE>
 __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__restrict__ A,
                                                       int64_t lda, T *__restrict__ W, int ldw,
                                                       int npanels) {
@@ -121,9 +125,16 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
     // return zero (they only reach rows and columns >= bs, which are unused).
     const int64_t doff = base + base * lda;
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(A + doff, ((m - 1) + (m - 1) * lda + 1 - doff) * (int64_t)sizeof(T));
-    auto col_off = [&](int k) -> uint32_t {
-        return (uint32_t)(((int64_t)row0 + (int64_t)k * lda) * (int64_t)sizeof(T));
+        make_rsrc(A + doff, WIDE ? 0 : ((m - 1) + (m - 1) * lda + 1 - doff) * (int64_t)sizeof(T));
+    // rows row0 .. row0+R-1 of column k of D; past the block they read zero
+    auto load_col = [&](int k, T (&dst)[R]) {
+        if constexpr (WIDE) {
+            const __amdgpu_buffer_rsrc_t rc =
+                make_rsrc(A + doff + (int64_t)k * lda, k < bs ? (int64_t)bs * (int64_t)sizeof(T) : 0);
+            ld_elems<T, R, VEC>(rc, (uint32_t)(row0 * (int)sizeof(T)), dst);
+        } else {
+            ld_elems<T, R, VEC>(rs, (uint32_t)(((int64_t)row0 + (int64_t)k * lda) * (int64_t)sizeof(T)), dst);
+        }
     };
 
     // identity tile E_j for columns j0 .. j0+P-1, and reciprocals of own pivots
@@ -133,7 +144,10 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
     for (int rr = 0; rr < R; ++rr) {
         const int i = row0 + rr;
         T d[1];
-        ld_elems<T, 1, false>(rs, (uint32_t)(((int64_t)i + (int64_t)i * lda) * (int64_t)sizeof(T)), d);
+        if constexpr (WIDE)
+            d[0] = i < bs ? A[doff + (int64_t)i + (int64_t)i * lda] : E::one();
+        else
+            ld_elems<T, 1, false>(rs, (uint32_t)(((int64_t)i + (int64_t)i * lda) * (int64_t)sizeof(T)), d);
         inv[rr] = E::recip(d[0]);
 #pragma unroll
         for (int jj = 0; jj < P; ++jj) x[rr][jj] = E::sel(i == j0 + jj, E::one(), E::zero());
@@ -146,7 +160,7 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
     const int k_begin = (j0 / U) * U;
     T ring[DP][R];
 #pragma unroll
-    for (int u = 0; u < DP; ++u) ld_elems<T, R, VEC>(rs, col_off(k_begin + u), ring[u]);
+    for (int u = 0; u < DP; ++u) load_col(k_begin + u, ring[u]);
     for (int k0 = k_begin; k0 < bs; k0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -187,7 +201,7 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(int64_t m, const T *__rest
 #pragma unroll
                 for (int jj = 0; jj < P; ++jj) x[r][jj] = E::sel(own, s[jj], x[r][jj]);
             }
-            ld_elems<T, R, VEC>(rs, col_off(k + DP), ring[slot]);  // refill the slot just used
+            load_col(k + DP, ring[slot]);  // refill the slot just used
         }
     }
 
@@ -213,16 +227,22 @@ hipError_t launch_r(int64_t m, const void *A, int64_t lda, void *W, int ldw, hip
     if (total > 0x7fffffffLL - 8) return hipErrorInvalidConfiguration;
     if (ldw % IB != 0) return hipErrorInvalidValue;
     const int64_t grid = 8 * ((total + 7) / 8);  // whole rounds over the 8 XCDs
-    // 32-bit buffer offsets reach one diagonal block: IB columns of lda
-    if ((int64_t)sizeof(T) * (lda + 1) * IB > 0x7fffffffLL) return hipErrorInvalidValue;
+    // one buffer resource reaches a whole diagonal block (IB columns of lda)
+    // while that spans less than 2 GB; beyond, one resource per column
+    const bool wide = (int64_t)sizeof(T) * (lda + 1) * IB > 0x7fffffffLL;
     const int vec = (reinterpret_cast<uintptr_t>(A) % 16 == 0) &&
                     ((int64_t)sizeof(T) * lda) % 16 == 0;
-    if (vec)
-        hipLaunchKernelGGL((diag_inv_kernel<T, R, P, true>), dim3((unsigned)grid), dim3(64), 0, st, m,
-                           static_cast<const T *>(A), lda, static_cast<T *>(W), ldw, npanels);
+    const T *a = static_cast<const T *>(A);
+    T *w = static_cast<T *>(W);
+    const dim3 g((unsigned)grid);
+    if (wide && vec)
+        hipLaunchKernelGGL((diag_inv_kernel<T, R, P, true, true>), g, dim3(64), 0, st, m, a, lda, w, ldw, npanels);
+    else if (wide)
+        hipLaunchKernelGGL((diag_inv_kernel<T, R, P, false, true>), g, dim3(64), 0, st, m, a, lda, w, ldw, npanels);
+    else if (vec)
+        hipLaunchKernelGGL((diag_inv_kernel<T, R, P, true, false>), g, dim3(64), 0, st, m, a, lda, w, ldw, npanels);
     else
-        hipLaunchKernelGGL((diag_inv_kernel<T, R, P, false>), dim3((unsigned)grid), dim3(64), 0, st, m,
-                           static_cast<const T *>(A), lda, static_cast<T *>(W), ldw, npanels);
+        hipLaunchKernelGGL((diag_inv_kernel<T, R, P, false, false>), g, dim3(64), 0, st, m, a, lda, w, ldw, npanels);
     return hipGetLastError();
 }
 

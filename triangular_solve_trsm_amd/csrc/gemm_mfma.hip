@@ -214,7 +214,11 @@ __device__ __forceinline__ void store_rows4(R *X, int64_t ld, int64_t lim, int64
 // BLO: Bm is lower triangular (explicit zeros above its diagonal), as the
 // right factor of the inversion's second product: a column tile starting at
 // column j0 skips the K tiles wholly above row j0.
-template <typename T, int MT, int NT, int KT, bool TRI, bool VEC, bool BLO = false>
+// WIDE: A and Bm are read through 64-bit global addresses (ld16_wide) instead
+// of 32-bit buffer offsets, for leading dimensions so large that the offsets
+// inside one tile would not fit (fp64: lda beyond about 8 M elements, or ldb
+// beyond about 2 M on the widest tile); only the 64 x 32 tile has this form.
+template <typename T, int MT, int NT, int KT, bool TRI, bool VEC, bool BLO = false, bool WIDE = false>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     using Tr = GemmTraits<T>;
     using R = typename Tr::R;
@@ -372,29 +376,35 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
             const int64_t k0t = CPLX ? k0 / 2 : k0;
             {
                 const int64_t off = i0t + k0t * p.lda;
-                const __amdgpu_buffer_rsrc_t rs =
-                    make_rsrc(pA + off, live ? (p.extA - off) * (int64_t)sizeof(T) : 0);
+                const int64_t lim = live ? (p.extA - off) * (int64_t)sizeof(T) : 0;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(pA + off, WIDE ? 0 : lim);
 #pragma unroll
                 for (int s = 0; s < A_PASSES; ++s) {
                     const int flat = s * 256 + tid;
                     const int kk = flat / A_TPC;
                     const int rr = flat - kk * A_TPC;
-                    const uint32_t boff = (uint32_t)(((int64_t)rr * AU + (int64_t)kk * p.lda) * (int64_t)sizeof(T));
-                    ra[S][s] = ld16<VEC>(rs, boff);
+                    const int64_t boff = ((int64_t)rr * AU + (int64_t)kk * p.lda) * (int64_t)sizeof(T);
+                    if constexpr (WIDE)
+                        ra[S][s] = ld16_wide(reinterpret_cast<const char *>(pA + off), boff, lim);
+                    else
+                        ra[S][s] = ld16<VEC>(rs, (uint32_t)boff);
                 }
             }
             {
                 const int64_t off = k0t + j0 * p.ldb;
-                const __amdgpu_buffer_rsrc_t rs =
-                    make_rsrc(pB + off, live ? (p.extB - off) * (int64_t)sizeof(T) : 0);
+                const int64_t lim = live ? (p.extB - off) * (int64_t)sizeof(T) : 0;
+                const __amdgpu_buffer_rsrc_t rs = make_rsrc(pB + off, WIDE ? 0 : lim);
 #pragma unroll
                 for (int s = 0; s < B_PASSES; ++s) {
                     const int flat = s * 256 + tid;
                     const int jj = flat / B_TPC;
                     const int kv = (flat - jj * B_TPC) * VR;  // real k inside the tile
                     const int64_t kvt = CPLX ? kv / 2 : kv;
-                    const uint32_t boff = (uint32_t)((kvt + (int64_t)jj * p.ldb) * (int64_t)sizeof(T));
-                    rb[S][s] = ld16<VEC>(rs, boff);
+                    const int64_t boff = (kvt + (int64_t)jj * p.ldb) * (int64_t)sizeof(T);
+                    if constexpr (WIDE)
+                        rb[S][s] = ld16_wide(reinterpret_cast<const char *>(pB + off), boff, lim);
+                    else
+                        rb[S][s] = ld16<VEC>(rs, (uint32_t)boff);
                 }
             }
         };
@@ -581,10 +591,12 @@ inline bool aligned16(const void *ptr, int64_t ld, size_t es) {
     return (reinterpret_cast<uintptr_t>(ptr) % 16) == 0 && ((int64_t)es * ld) % 16 == 0;
 }
 
-template <typename T, int MT, int NT, int KT>
-hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
+// Kernel parameters and grid of descriptor g on an MT x NT tile.  Returns
+// hipSuccess with grid.x == 0 when there is nothing to compute.
+template <typename T, int MT, int NT>
+hipError_t tile_params(const GemmDesc &g, GemmParams<T> &p, dim3 &grid) {
     constexpr bool CPLX = GemmTraits<T>::kCplx;
-    GemmParams<T> p;
+    grid = dim3(0u, 1u, 1u);
     p.M = g.M;
     p.N = g.N;
     p.K = g.K;
@@ -649,7 +661,16 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
         if (!al(g.sDo, g.sDi)) p.d_vec = p.d2_vec = 0;
     }
     const int64_t rowsM = p.fold ? (tM + 1) / 2 : tM;  // folded triangle: pairs of row tiles
-    const dim3 grid((unsigned)(rowsM * tN), (unsigned)nz);
+    grid = dim3((unsigned)(rowsM * tN), (unsigned)nz);
+    return hipSuccess;
+}
+
+template <typename T, int MT, int NT, int KT>
+hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
+    GemmParams<T> p;
+    dim3 grid;
+    hipError_t e = tile_params<T, MT, NT>(g, p, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
     const bool vec = p.a_vec && p.b_vec;
     if (g.b_lower) {
         // the shapes launched with it (the inversion's second product)
@@ -666,6 +687,23 @@ hipError_t launch_tile(const GemmDesc &g, hipStream_t st) {
         if (vec) hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, false, true>), grid, dim3(256), 0, st, p);
         else hipLaunchKernelGGL((gemm_kernel<T, MT, NT, KT, false, false>), grid, dim3(256), 0, st, p);
     }
+    return hipGetLastError();
+}
+
+// Operands whose leading dimension is too large for 32-bit buffer offsets
+// inside a tile: the 64 x 32 tile with 64-bit global loads (WIDE).
+template <typename T, int KT>
+hipError_t launch_wide(const GemmDesc &g, hipStream_t st) {
+    GemmParams<T> p;
+    dim3 grid;
+    hipError_t e = tile_params<T, 64, 32>(g, p, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    if (g.b_lower)
+        hipLaunchKernelGGL((gemm_kernel<T, 64, 32, KT, false, false, true, true>), grid, dim3(256), 0, st, p);
+    else if (g.a_lower)
+        hipLaunchKernelGGL((gemm_kernel<T, 64, 32, KT, true, false, false, true>), grid, dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<T, 64, 32, KT, false, false, false, true>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -836,10 +874,20 @@ hipError_t gemm_splitk_launch(int dtype, const GemmDesc &g, int parts, void *par
 hipError_t gemm_launch(int dtype, const GemmDesc &g, hipStream_t stream) {
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     if (g.a_lower && g.b_lower) return hipErrorInvalidValue;
-    // 32-bit buffer offsets inside one K tile of A and one column tile of Bm
+    // Buffer loads take 32-bit offsets from a tile's first element: they
+    // reach the 32 (fp32) or 16 K columns of an A tile and the up to 128
+    // columns of a Bm tile only while those span less than 2 GB.  Beyond
+    // that the 64 x 32 tile runs with 64-bit addresses.
     const int64_t es = (int64_t)dtype_size(dtype);
-    if (g.lda * es * 32 + 4096 > 0x7fffffffLL || g.ldb * es * 128 + 4096 > 0x7fffffffLL)
-        return hipErrorInvalidValue;
+    if (g.lda > (0x7fffffffLL - 4096) / (es * 32) || g.ldb > (0x7fffffffLL - 4096) / (es * 128)) {
+        switch (dtype) {
+            case R32F: return launch_wide<float, 32>(g, stream);
+            case R64F: return launch_wide<double, 16>(g, stream);
+            case C64F: return launch_wide<cplx, 16>(g, stream);
+            case C32F: return launch_wide<cplx32, 32>(g, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (dtype) {
         case R32F: return launch_sized<float, 32>(g, stream);
         case R64F: return launch_sized<double, 16>(g, stream);
