@@ -146,6 +146,34 @@ trsm_status_t trsm_solve(trsm_side_t side, trsm_fill_t uplo, trsm_op_t trans, tr
                          const void *A, int64_t lda, void *B, int64_t ldb, hipStream_t stream);
 
 /*
+ * trsm_lln for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that must not call hipMalloc, harnesses that
+ * forbid allocation.  Same arguments, results and quick returns as
+ * trsm_lln (the same kernels with the same block size, so X is bitwise that
+ * of trsm_lln).  The blocked path's workspace (m > 64) comes from a fixed
+ * array in the library's device memory, TRSM_NOALLOC_MAX_WORKSPACE_BYTES
+ * per device, held from library load until the process ends; the call
+ * performs no allocation of any kind.
+ * A problem whose workspace exceeds that size returns
+ * TRSM_STATUS_INVALID_VALUE before any HIP call, with B untouched.  The
+ * workspace is nb*ib*ib elements of inverses plus max(ib*n, the
+ * inversion's scratch) elements of panel plus split-K partial sums (at
+ * most 2^21 elements), each rounded up to 256 bytes, with ib and nb =
+ * ceil(m/ib) from trsm_lln_select_ib; e.g. fp64 m = n = 8192 (ib 1024)
+ * needs 128 MiB and fits, complex fp64 8192 x 2048 needs 160 MiB and does
+ * not.  m <= 64 and alpha == 0 need no workspace at all.
+ * Every call on one device shares that device's array and leaves its
+ * contents behind (nothing in it needs to start at zero): calls whose
+ * kernels may overlap in time on one device -- on different streams, or
+ * from several host threads without ordering -- race on it and give wrong
+ * results.  Calls ordered on one stream are safe.
+ */
+#define TRSM_NOALLOC_MAX_WORKSPACE_BYTES (128ull << 20)
+trsm_status_t trsm_lln_noalloc(trsm_dtype_t dtype, int64_t m, int64_t n, const void *alpha,
+                               const void *A, int64_t lda, void *B, int64_t ldb,
+                               hipStream_t stream);
+
+/*
  * Block size the blocked path uses for (dtype, m, n): nearest-scale match
  * in the table built by offline profiling on MI355X (section 4.3.2), the
  * scale being (m, n) compared in log space (the table holds square

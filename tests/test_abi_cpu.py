@@ -212,3 +212,20 @@ def test_python_binding_rejects_host_tensors(T):
         with pytest.raises(ValueError, match="GPU tensor"):
             call_()
 
+
+def test_noalloc_refuses_before_any_hip_call(T):
+    """trsm_lln_noalloc checks its arguments like trsm_lln, and refuses a
+    problem whose blocked-path workspace exceeds its fixed scratch array
+    (TRSM_NOALLOC_MAX_WORKSPACE_BYTES) before any HIP call: with no GPU here,
+    a HIP call would fail with HIP_ERROR instead of INVALID_VALUE."""
+    al = T.alpha_buffer(1, 1.0)
+    a = ctypes.addressof(al)
+    f = T.lib.trsm_lln_noalloc
+    assert f(1, 4, 3, a, FAKE, 3, FAKE, 4, None) == 1          # lda < m
+    assert f(7, 4, 3, a, FAKE, 4, FAKE, 4, None) == 1          # dtype
+    assert f(1, 0, 3, a, None, 1, None, 1, None) == 0          # m == 0
+    # m = 65, n = 2^21 fp64: the panel alone is ib * n * 8 >= 1 GiB
+    assert f(1, 65, 1 << 21, a, FAKE, 65, FAKE, 65, None) == 1
+    # complex fp64 8192 x 2048 (ib 1024): 128 MiB of inverses + 32 MiB of panel
+    alz = T.alpha_buffer(2, 1.0)
+    assert f(2, 8192, 2048, ctypes.addressof(alz), FAKE, 8192, FAKE, 8192, None) == 1

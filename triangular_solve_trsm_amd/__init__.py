@@ -7,6 +7,7 @@ kernels.  The functions carry the names of the C ABI (include/trsm.h):
     trsm_solve(A, B, alpha=1.0, *, side, uplo, trans, diag, stream=None) -> B
     trsm_lln_strided_batched(A, B, alpha=1.0, *, stream=None)      -> B
     trsm_lln_ex(A, B, alpha=1.0, ib=0, force_blocked=False, *, stream=None) -> B
+    trsm_lln_noalloc(A, B, alpha=1.0, *, stream=None)              -> B
     trsm_lln_select_ib(dtype, m, n)                                -> int
     trsm_status_string(status)                                     -> str
     trsm_release_workspace()
@@ -35,7 +36,8 @@ STATUS = {0: "SUCCESS", 1: "INVALID_VALUE", 2: "ALLOC_FAILED", 3: "HIP_ERROR", 4
 IB_CHOICES = (64, 128, 256, 512, 1024)
 
 # Every symbol include/trsm.h and include/trsm_kernels.h declare.
-EXPORTS = ("trsm_lln", "trsm_solve", "trsm_lln_strided_batched", "trsm_lln_ex", "trsm_lln_select_ib",
+EXPORTS = ("trsm_lln", "trsm_solve", "trsm_lln_strided_batched", "trsm_lln_ex", "trsm_lln_noalloc",
+           "trsm_lln_select_ib",
            "trsm_status_string", "trsm_release_workspace",
            "trsm_kernel_diag_inv", "trsm_kernel_gemm",
            "trsm_profile_start", "trsm_profile_stop", "trsm_profile_count", "trsm_profile_read")
@@ -67,6 +69,8 @@ def _load() -> ctypes.CDLL:
     lib.trsm_lln_strided_batched.argtypes = [ci, i64, i64, vp, vp, i64, i64, vp, i64, i64, i64, vp]
     lib.trsm_lln_strided_batched.restype = ci
     lib.trsm_lln_ex.argtypes = [ci, i64, i64, vp, vp, i64, vp, i64, ci, ci, vp]
+    lib.trsm_lln_noalloc.argtypes = [ci, i64, i64, vp, vp, i64, vp, i64, vp]
+    lib.trsm_lln_noalloc.restype = ci
     lib.trsm_solve.argtypes = [ci, ci, ci, ci, ci, i64, i64, vp, vp, i64, vp, i64, vp]
     lib.trsm_solve.restype = ci
     lib.trsm_lln_ex.restype = ci
@@ -191,6 +195,29 @@ def trsm_lln(A, B, alpha=1.0, *, stream=None):
     st = lib.trsm_lln(code, m, n, ctypes.addressof(al), A.data_ptr(), lda, B.data_ptr(), ldb,
                       _stream_handle(stream))
     _check(st, "trsm_lln")
+    return B
+
+
+NOALLOC_MAX_WORKSPACE_BYTES = 128 << 20  # TRSM_NOALLOC_MAX_WORKSPACE_BYTES of trsm.h
+
+
+def trsm_lln_noalloc(A, B, alpha=1.0, *, stream=None):
+    """trsm_lln without any allocation: the blocked path's workspace is the
+    library's fixed per-device scratch array (NOALLOC_MAX_WORKSPACE_BYTES);
+    larger problems raise TrsmError (INVALID_VALUE) with B untouched.  Calls
+    that may overlap in time on one device race on that array."""
+    code = _dtype_code(B)
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    m, n = B.shape
+    if tuple(A.shape) != (m, m):
+        raise ValueError(f"A must be {m} x {m}")
+    lda, ldb = _ld(A, m, m), _ld(B, m, n)
+    _check_device("trsm_lln_noalloc", A, B, stream=stream)
+    al = alpha_buffer(code, alpha)
+    st = lib.trsm_lln_noalloc(code, m, n, ctypes.addressof(al), A.data_ptr(), lda, B.data_ptr(), ldb,
+                              _stream_handle(stream))
+    _check(st, "trsm_lln_noalloc")
     return B
 
 

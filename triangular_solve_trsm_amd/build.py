@@ -27,7 +27,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "small_lln.hip", "small_mfma.hip", "diag_inv.hip", "gemm_mfma.hip", "aux_kernels.hip"]
+SOURCES = ["api.cpp", "small_lln.hip", "small_mfma.hip", "diag_inv.hip", "gemm_mfma.hip", "aux_kernels.hip",
+           "noalloc.hip"]
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -496,6 +496,42 @@ trsm_status_t trsm_lln(trsm_dtype_t dtype, int64_t m, int64_t n, const void *alp
     }
 }
 
+trsm_status_t trsm_lln_noalloc(trsm_dtype_t dtype, int64_t m, int64_t n, const void *alpha,
+                               const void *A, int64_t lda, void *B, int64_t ldb,
+                               hipStream_t stream) {
+    try {
+        trsm_status_t s = check_args(dtype, m, n, alpha, A, lda, B, ldb);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        if (m == 0 || n == 0) return TRSM_STATUS_SUCCESS;
+        const Scalar al = read_alpha(dtype, alpha);
+        const bool direct = m <= 64 || (al.re == 0.0 && al.im == 0.0);
+        // the blocked path's plan and its workspace size: host arithmetic only,
+        // so an oversized problem is refused before any HIP call
+        BlockedPlan pl;
+        if (!direct) {
+            const IbEntry cfg = select_entry(dtype, m, n);
+            pl = plan_blocked(dtype, m, n, cfg.ib, cfg.left != 0);
+            if (pl.bytes() > (size_t)TRSM_NOALLOC_MAX_WORKSPACE_BYTES) {
+                if (log_enabled())
+                    std::fprintf(stderr, "[trsm] noalloc: workspace %zu bytes > %llu\n", pl.bytes(),
+                                 (unsigned long long)TRSM_NOALLOC_MAX_WORKSPACE_BYTES);
+                return TRSM_STATUS_INVALID_VALUE;
+            }
+        }
+        if (direct) return run(dtype, m, n, alpha, A, lda, 0, B, ldb, 0, 1, 0, false, stream);
+        int dev = 0;
+        s = check_device(&dev);
+        if (s != TRSM_STATUS_SUCCESS) return s;
+        void *ws = nullptr;
+        size_t ws_bytes = 0;
+        if (noalloc_scratch(dev, &ws, &ws_bytes) != hipSuccess) return TRSM_STATUS_HIP_ERROR;
+        if (pl.bytes() > ws_bytes) return TRSM_STATUS_INVALID_VALUE;
+        return exec_blocked(pl, dtype, m, n, al, A, lda, B, ldb, ws, stream);
+    } catch (...) {
+        return TRSM_STATUS_HIP_ERROR;
+    }
+}
+
 trsm_status_t trsm_lln_strided_batched(trsm_dtype_t dtype, int64_t m, int64_t n,
                                        const void *alpha, const void *A, int64_t lda,
                                        int64_t strideA, void *B, int64_t ldb, int64_t strideB,

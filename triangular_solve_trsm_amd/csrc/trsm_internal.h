@@ -124,6 +124,12 @@ hipError_t copy_panel_launch(int dtype, int64_t rows, int64_t n, const void *src
 struct Reflect {
     int revR, revC, trans, conj, lower, unit;
 };
+// ---- fixed scratch of trsm_lln_noalloc (noalloc.hip) ------------------------
+// Device address of the current device `dev`'s copy of the library's static
+// scratch array (TRSM_NOALLOC_MAX_WORKSPACE_BYTES), taken on the first call
+// for that device; *bytes receives its size.
+hipError_t noalloc_scratch(int dev, void **out, size_t *bytes);
+
 hipError_t transform_launch(int dtype, int64_t R, int64_t C, const void *src, int64_t lds,
                             void *dst, int64_t ldd, const Reflect &f, hipStream_t stream);
 
