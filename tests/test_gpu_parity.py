@@ -79,8 +79,20 @@ def test_c2_batched_c64_64(T):
     assert e <= TOL["c64"] and e <= SANITY["c64"], e
 
 
+def tile_columns(n, width=64):
+    """One column in every `width`-column tile of B (its position inside the
+    tile varies, so every lane position of the GEMM tiles is met), plus the
+    last column."""
+    cols = [t * width + (t * 37) % width for t in range((n + width - 1) // width)]
+    return np.unique(np.array([c for c in cols if c < n] + [n - 1]))
+
+
 @pytest.mark.parametrize("name", ["c3_f32_4096", "c4_f64_8192", "c5_c64_8192x2048"])
-def test_large_workloads_sampled_and_residual(T, name):
+def test_large_workloads_vs_oracle_and_residual(T, name):
+    """C3 is compared with the oracle on its whole output; C4 and C5 on one
+    column of every 64-column tile plus the last (columns are independent
+    problems), 129 and 33 columns.  The whole output of each also goes
+    through the residual bound."""
     import torch
     cfg = CONFIGS[name]
     L, B, a = make_config(cfg)
@@ -88,10 +100,13 @@ def test_large_workloads_sampled_and_residual(T, name):
     B0 = Bd.clone()
     T.trsm_lln(Ad, Bd, a)
     sync()
-    cols = np.unique(np.linspace(0, cfg.n - 1, 8).astype(int))
-    Xs = from_dev(Bd[:, torch.as_tensor(cols, device=Bd.device)])
-    ref = oracle.solve(L, np.asfortranarray(B[:, cols]), a)
-    check(cfg.dtype, Xs, ref, name)
+    if name == "c3_f32_4096":
+        check(cfg.dtype, from_dev(Bd), oracle.solve(L, B, a), name + " (whole output)")
+    else:
+        cols = tile_columns(cfg.n)
+        Xs = from_dev(Bd[:, torch.as_tensor(cols, device=Bd.device)])
+        ref = oracle.solve(L, np.asfortranarray(B[:, cols]), a)
+        check(cfg.dtype, Xs, ref, f"{name} ({len(cols)} columns)")
     # residual of the whole output, computed on the GPU in float64/complex128
     wide = torch.complex128 if cfg.dtype == "c64" else torch.float64
     Lw = torch.tril(Ad.to(wide))
@@ -364,7 +379,7 @@ def test_non_finite_b_entry_stays_in_its_column(T, dtype, m, n, ib):
         check(dtype, col[start:k][fin], rcol[start:k][fin], f"{dtype} m={m}: finite rows of the NaN's block")
 
 
-@pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_deterministic(T, dtype):
     L, B = make_problem(dtype, 900, 300, seed=5)
     X1 = solve_gpu(T, L, B, 1.0)
@@ -416,14 +431,15 @@ def test_workspace_allocation_failure_leaves_B_untouched(T, monkeypatch):
     T.trsm_release_workspace()
 
 
-# ---- the streaming batched kernel (>= 2 tasks per CU, fp64 / complex) -------
+# ---- large batches: many resident workgroups per CU (fp64 / complex) --------
 
 @pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
 @pytest.mark.parametrize("batch,m,n", [(600, 64, 64), (600, 1, 64), (600, 17, 5), (520, 33, 100),
                                        (2100, 64, 64), (300, 48, 130)])
-def test_batched_streaming(T, dtype, batch, m, n):
-    """Enough tasks (problem x 64-column group) for the persistent streaming
-    kernel; ragged m, several column groups, more tasks than waves."""
+def test_batched_many_workgroups(T, dtype, batch, m, n):
+    """Enough workgroups (problem x 64-column group) for several to be
+    resident on every CU at once and for more than one round; ragged m,
+    several column groups."""
     L, B = make_problem(dtype, m, n, seed=batch + 7 * m + n, batch=batch)
     a = 0.5 - 0.25j if dtype in CPLX else -0.75
     Ad, Bd = to_dev(L), to_dev(B)
@@ -436,7 +452,7 @@ def test_batched_streaming(T, dtype, batch, m, n):
 
 
 @pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
-def test_batched_streaming_padded_nan_upper(T, dtype):
+def test_batched_many_padded_nan_upper(T, dtype):
     """Padded leading dimensions, a NaN strict upper triangle and NaN padding
     in A; B's padding rows must stay untouched."""
     import torch
@@ -456,9 +472,9 @@ def test_batched_streaming_padded_nan_upper(T, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f64", "c64", "c32"])
-def test_batched_streaming_bidiagonal_exact(T, dtype):
+def test_batched_many_bidiagonal_exact(T, dtype):
     """Unit bidiagonal L with -1 below the diagonal on every problem: X is the
-    running column sum of integer B, exact on the streaming path."""
+    running column sum of integer B, exact on the batched direct path."""
     batch, m, n = 600, 64, 64
     L1 = unit_bidiagonal_minus_one(m, dtype)
     L = np.ascontiguousarray(np.broadcast_to(L1, (batch, m, m)).transpose(0, 2, 1)).transpose(0, 2, 1)
@@ -468,3 +484,79 @@ def test_batched_streaming_bidiagonal_exact(T, dtype):
     T.trsm_lln_strided_batched(Ad, Bd, 1.0)
     sync()
     assert np.array_equal(from_dev(Bd), np.cumsum(B, axis=1))
+
+
+# ---- guard regions around B ----------------------------------------------------
+
+GUARD = 4096  # elements before and after B's storage
+
+
+def guarded(a, ld, batch_stride=None):
+    """Device buffer holding [GUARD sentinels][B storage][GUARD sentinels];
+    returns (view of B, buffer, first element past B's storage)."""
+    import torch
+    dt = torch_dtype({np.float32: "f32", np.float64: "f64", np.complex128: "c64",
+                      np.complex64: "c32"}[a.dtype.type])
+    if a.ndim == 2:
+        m, n = a.shape
+        size = ld * n
+    else:
+        b, m, n = a.shape
+        size = batch_stride * (b - 1) + ld * n
+    buf = torch.full((GUARD + size + GUARD,), 4321.0, dtype=dt, device="cuda")
+    if a.ndim == 2:
+        view = torch.as_strided(buf, (m, n), (1, ld), GUARD)
+    else:
+        view = torch.as_strided(buf, (a.shape[0], m, n), (batch_stride, 1, ld), GUARD)
+    view.copy_(torch.from_numpy(np.ascontiguousarray(a)).to("cuda"))
+    return view, buf, GUARD + size
+
+
+def guards_intact(buf, end):
+    import torch
+    return bool(torch.all(buf[:GUARD] == 4321.0).item()) and bool(torch.all(buf[end:] == 4321.0).item())
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
+@pytest.mark.parametrize("m,n,ib", [(64, 64, 0), (37, 130, 0), (700, 90, 128), (1000, 257, 0),
+                                    (2100, 48, 512)])
+def test_guard_regions_around_b_untouched(T, dtype, m, n, ib):
+    """Nothing is written before B's first element or after its last one
+    (element ldb*(n-1) + m - 1 and the padding after it) on the direct path,
+    the blocked path (ragged tiles, split K at n = 48) and every type."""
+    L, B = make_problem(dtype, m, n, seed=300 + m + n)
+    a = 0.5 - 0.25j if dtype in CPLX else 0.5
+    Ad = to_dev(L)
+    Bd, buf, end = guarded(B, m + 3)
+    if ib:
+        T.trsm_lln_ex(Ad, Bd, a, ib=ib)
+    else:
+        T.trsm_lln(Ad, Bd, a)
+    sync()
+    assert guards_intact(buf, end), f"{dtype} m={m} n={n}: a guard region was written"
+    check(dtype, from_dev(Bd), oracle.solve(L, B, a), f"{dtype} m={m} n={n} guarded")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
+@pytest.mark.parametrize("batch,m,n", [(9, 64, 64), (5, 33, 70), (3, 150, 20)])
+def test_guard_regions_around_batched_b_untouched(T, dtype, batch, m, n):
+    """Batched problems at a stride with a gap after each problem's B: the
+    gaps and the regions before the first and after the last problem keep
+    their sentinels."""
+    import torch
+    L, B = make_problem(dtype, m, n, seed=batch + m, batch=batch)
+    ldb = m + 2
+    stride = ldb * n + 100
+    Ad = to_dev(L)
+    Bd, buf, end = guarded(B, ldb, stride)
+    T.trsm_lln_strided_batched(Ad, Bd, 1.0)
+    sync()
+    assert guards_intact(buf, end)
+    body = buf[GUARD:end]
+    for p in range(batch - 1):  # the 100 elements after each problem but the last
+        gap = body[p * stride + ldb * n: (p + 1) * stride]
+        assert bool(torch.all(gap == 4321.0).item()), f"gap after problem {p} was written"
+    full = from_dev(torch.as_strided(buf, (batch, ldb, n), (stride, 1, ldb), GUARD))
+    assert np.all(full[:, m:] == 4321.0), "padding rows of B were modified"
+    e = max_problem_nrel(full[:, :m], oracle.solve_batched(L, B, 1.0))
+    assert e <= TOL[dtype] and e <= SANITY[dtype], e

@@ -54,7 +54,8 @@ hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t 
 // ---- kernels (b2, b3): MFMA GEMM -----------------------------------------
 //   D = beta * C + gamma * (A * Bm)
 // A: M x K (lda), Bm: K x N (ldb), C/D: M x N, all column-major.
-// Output rows [0, split) go to D2 (ldd2) instead of D (ldd); split % 16 == 0.
+// Output rows [0, split) go to D2 (ldd2) instead of D (ldd); any 0 <= split <= M
+// (a ragged last block row routes fewer than ib rows).
 // C may alias D (in place).  beta == 0 means C is not read (may be null).
 // a_lower != 0: A is lower triangular (explicit zeros above the diagonal);
 // K-tiles to the right of a row tile's diagonal are skipped (requires M == K).
