@@ -17,8 +17,14 @@ Reported (one JSON line on stdout):
                recorded on the launch stream during the timed steps, against
                the MI355X fp64 matrix peak;
   parts        the same per workload and per kernel, including the batched
-               kernel's effective HBM bandwidth against 8 TB/s;
-  cpu_baseline the CPU oracle timed on a bounded sample of the same workloads.
+               kernel's effective HBM bandwidth against 8 TB/s; after the
+               timed steps, the other configurations (fp64 64 x 64; fp32
+               4096^2, alpha 0.5; complex fp64 8192 x 2048) and the fp64
+               8192^2 solve at every block size, each by the pages' protocol
+               (one warm-up, mean of the next 9) with the per-phase split of
+               the pages' Table 3;
+  cpu_baseline the CPU oracle timed on a bounded sample of the same workloads,
+               on all host threads and (C1, C2 sample) on one core.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -60,8 +66,8 @@ def kernel_algorithmic(rec):
     """(flops, bytes) of one launch by its record, counted algorithmically:
     GEMM 2MNK (x4 complex); triangular solve GEMM M(M+1)N (x4 complex);
     small kernel: triangle of L + B read + X written per problem."""
-    cplx = rec["dtype"] == 2
-    es = {0: 4, 1: 8, 2: 16}[rec["dtype"]]
+    cplx = rec["dtype"] in (2, 3)
+    es = {0: 4, 1: 8, 2: 16, 3: 8}[rec["dtype"]]
     f = 4.0 if cplx else 1.0
     m, n, k, b = rec["m"], rec["n"], rec["k"], rec["batch"]
     if rec["kind"] == "update_gemm":
@@ -82,7 +88,7 @@ def summarize_kernels(records):
     out = {}
     for r in records:
         fl, by = kernel_algorithmic(r)
-        d = out.setdefault(r["kind"] + ("_c64" if r["dtype"] == 2 else "_f64" if r["dtype"] == 1 else "_f32"),
+        d = out.setdefault(r["kind"] + {0: "_f32", 1: "_f64", 2: "_c64", 3: "_c32"}[r["dtype"]],
                            {"launches": 0, "ms": 0.0, "flops": 0.0, "bytes": 0.0})
         d["launches"] += 1
         d["ms"] += r["ms"]
@@ -188,6 +194,156 @@ def measured_traffic(kernel_key):
     return rec["bytes_per_launch"]
 
 
+PHASES = {"diag_inv": "diagonal inversion", "update_gemm": "GEMM update", "solve_gemm": "solve GEMM",
+          "copy": "copy", "small": "direct solve", "fill": "zero fill"}
+
+
+def protocol_time(T, call, restore, warm_s=0.3, runs=9):
+    """The pages' protocol (HSMA-TRSM section 5.1: one warm-up run, then the
+    mean of the next 9), after a sustained warm-up of about warm_s seconds of
+    the same call (the GPU clock drops while the host prepares inputs).  B is
+    restored from a pristine copy outside the timed events.  Also returns the
+    launch records of the timed runs (per-phase split, section 5.3.1
+    Table 3)."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        restore()
+        call()
+    restore()
+    call()  # the protocol's own warm-up run
+    torch.cuda.synchronize()
+    ts = []
+    T.trsm_profile_start()
+    for _ in range(runs):
+        restore()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    T.trsm_profile_stop()
+    return sum(ts) / len(ts), min(ts), T.profile_records()
+
+
+def phase_split(records):
+    """Share of kernel time per phase (diagonal inversion, GEMM update, solve
+    GEMM, copy), as the pages' Table 3 reports it."""
+    tot = sum(r["ms"] for r in records) or 1.0
+    out = {}
+    for r in records:
+        k = PHASES.get(r["kind"], r["kind"])
+        out[k] = out.get(k, 0.0) + r["ms"] / tot
+    return {k: round(v, 4) for k, v in out.items()}
+
+
+def time_other_configs(T, to_dev_fn, a4d, b4_host, a4, cfg4):
+    """C1, C3 and C5 on their own and C4 at every block size, by the pages'
+    protocol.  Returns bench 'parts' entries."""
+    import torch
+    from trsm_inputs import CONFIGS, make_config
+    parts = []
+    peak = {"f32": PEAK["fp32_mfma_tflops"], "f64": PEAK["fp64_mfma_tflops"], "c64": PEAK["fp64_mfma_tflops"]}
+
+    def entry(cfg, mean_ms, min_ms, recs, **extra):
+        tf = cfg.flops / (mean_ms * 1e-3) / 1e12
+        e = {"workload": cfg.name, "protocol": "1 warm-up + mean of 9", "mean_ms": mean_ms, "min_ms": min_ms,
+             "tflops": tf, f"frac_{'fp32' if cfg.dtype == 'f32' else 'fp64'}_mfma_peak": tf / peak[cfg.dtype]}
+        if cfg.m > 64:
+            e["phases"] = phase_split(recs)
+            kern = summarize_kernels(recs)
+            e["kernels"] = {k: {"mean_ms": v["mean_ms"], "launches_per_solve": v["launches"] / 9,
+                                "tflops": v["tflops"]} for k, v in kern.items()}
+        e.update(extra)
+        return e
+
+    for name in ("c1_f64_64", "c3_f32_4096", "c5_c64_8192x2048"):
+        cfg = CONFIGS[name]
+        log(f"{name}: inputs and timing")
+        L, B, a = make_config(cfg)
+        Ad, B0 = to_dev_fn(L), to_dev_fn(B)
+        Bd = B0.clone()
+        del L, B
+        mean_ms, min_ms, recs = protocol_time(T, lambda: T.trsm_lln(Ad, Bd, a), lambda: Bd.copy_(B0))
+        extra = {}
+        if cfg.m > 64:
+            extra["ib"] = T.trsm_lln_select_ib({"f32": T.R32F, "f64": T.R64F, "c64": T.C64F}[cfg.dtype],
+                                               cfg.m, cfg.n)
+        else:
+            # latency: back-to-back calls on the stream, solved in place
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(200):
+                T.trsm_lln(Ad, Bd, a)
+            e1.record()
+            torch.cuda.synchronize()
+            extra["us_per_call_back_to_back"] = e0.elapsed_time(e1) * 1e3 / 200
+        parts.append(entry(cfg, mean_ms, min_ms, recs, **extra))
+        del Ad, B0, Bd
+        torch.cuda.empty_cache()
+
+    # C4 at each block size of the sweep (section 4.3.2), the table's choice marked
+    B0 = to_dev_fn(b4_host)
+    Bd = B0.clone()
+    table_ib = T.trsm_lln_select_ib(T.R64F, cfg4.m, cfg4.n)
+    for ib in (64, 128, 256, 512, 1024):
+        log(f"{cfg4.name} at ib {ib}")
+        mean_ms, min_ms, recs = protocol_time(T, lambda: T.trsm_lln_ex(a4d, Bd, a4, ib=ib),
+                                              lambda: Bd.copy_(B0), warm_s=0.1)
+        parts.append(entry(cfg4, mean_ms, min_ms, recs, ib=ib, table_choice=(ib == table_ib)))
+    del B0, Bd
+    torch.cuda.empty_cache()
+    return parts
+
+
+SINGLE_CORE = r"""
+import json, sys, time
+sys.path.insert(0, {root!r})
+import numpy as np
+import oracle
+from trsm_inputs import CONFIGS, make_config
+out = {{"threads": oracle.num_threads()}}
+cfg = CONFIGS["c1_f64_64"]
+L, B, a = make_config(cfg)
+oracle.solve(L, B, a)
+reps, t = 0, time.perf_counter()
+while time.perf_counter() - t < {c1_s}:
+    oracle.solve(L, B, a)
+    reps += 1
+dt = time.perf_counter() - t
+out["c1"] = {{"gflops": cfg.flops * reps / dt / 1e9, "us_per_solve": dt / reps * 1e6, "solves": reps}}
+cfg = CONFIGS["c2_c64_64x64_b8192"]
+L, B, a = make_config(cfg)
+nb = {c2_problems}
+Ls, Bs = L[:nb], B[:nb]
+oracle.solve_batched(Ls, Bs, a)
+reps, t = 0, time.perf_counter()
+while time.perf_counter() - t < {c2_s}:
+    oracle.solve_batched(Ls, Bs, a)
+    reps += 1
+dt = time.perf_counter() - t
+fl = cfg.flops / cfg.batch * nb * reps
+out["c2"] = {{"gflops": fl / dt / 1e9, "solves_per_s": nb * reps / dt, "problems": nb, "repeats": reps}}
+print(json.dumps(out))
+"""
+
+
+def cpu_single_core(c1_s=1.5, c2_s=4.0, c2_problems=512):
+    """The oracle on one host core (OMP_NUM_THREADS=1, in a child process so
+    the thread count is fixed before OpenMP starts) on C1 and on the first
+    c2_problems problems of C2, repeated for about c1_s and c2_s seconds."""
+    import subprocess
+    code = SINGLE_CORE.format(root=ROOT, c1_s=c1_s, c2_s=c2_s, c2_problems=c2_problems)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        log(f"single-core oracle run failed: {r.stderr[-500:]}")
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +352,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled residual check")
     ap.add_argument("--ib", type=int, default=0, help="force the diagonal block size of the fp64 solve")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip timing C1, C3, C5 and the per-block-size C4 rows after the timed steps")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -311,11 +469,16 @@ def main():
          "roofline_bound": "hbm"},
     ]
 
+    if not args.no_other_configs:
+        parts += time_other_configs(T, to_dev, A4d, B4, a4, cfg4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         cpu = cpu_baseline((L4, B4, a4, cfg4), (L2, B2, a2, cfg2))
         log(f"cpu baseline: {cpu['value']:.2f} GFLOP/s on {cpu['cores']} threads")
+        log("cpu baseline on one core (C1, C2 sample)")
+        cpu["single_core"] = cpu_single_core()
 
     out = {
         "metric": METRIC,
