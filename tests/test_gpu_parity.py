@@ -560,3 +560,25 @@ def test_guard_regions_around_batched_b_untouched(T, dtype, batch, m, n):
     assert np.all(full[:, m:] == 4321.0), "padding rows of B were modified"
     e = max_problem_nrel(full[:, :m], oracle.solve_batched(L, B, 1.0))
     assert e <= TOL[dtype] and e <= SANITY[dtype], e
+
+
+@pytest.mark.parametrize("pc", ["0", "1"])
+@pytest.mark.parametrize("batch,m,n", [(1, 64, 64), (7, 33, 70), (300, 64, 64), (1000, 50, 130),
+                                       (257, 16, 1), (600, 64, 200)])
+def test_batched_complex_both_small_kernels(T, pc, batch, m, n, monkeypatch):
+    """Complex fp64 batches on each form of the direct solve, forced in
+    turn (TRSM_SMALL_PC): the workgroup-per-task kernel and the persistent
+    producer/consumer kernel (one workgroup per CU; a producer wave stages
+    the next task's L and B in LDS and inverts its diagonal blocks while
+    four MFMA waves solve the current task).  Fewer tasks than CUs, ragged m
+    and n, several column groups per problem, and more tasks than
+    workgroups."""
+    monkeypatch.setenv("TRSM_SMALL_PC", pc)
+    L, B = make_problem("c64", m, n, seed=batch + 3 * m + n, batch=batch, upper="nan")
+    a = 0.5 - 0.25j
+    Ad, Bd = to_dev(L), to_dev(B)
+    T.trsm_lln_strided_batched(Ad, Bd, a)
+    sync()
+    Lz, _ = make_problem("c64", m, n, seed=batch + 3 * m + n, batch=batch)
+    e = max_problem_nrel(from_dev(Bd), oracle.solve_batched(Lz, B, a))
+    assert e <= TOL["c64"] and e <= SANITY["c64"], e

@@ -30,6 +30,10 @@
 //     are read.
 // Four waves per workgroup and three (complex) or four (fp64) workgroups
 // per CU, so one workgroup's loads overlap the others' products.
+#include <cstdlib>
+#include <map>
+#include <mutex>
+
 #include "buffer_ops.h"
 #include "scalar_ops.h"
 
@@ -299,6 +303,227 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
     }
 }
 
+// ---- producer/consumer form for large batches of complex fp64 problems ----
+//
+// HSMA-TRSM, section 4.2.2 and Figure 5: for the complex fp64 case, whose
+// operands strain on-chip memory, the pages split each thread block into a
+// group that moves data and a group that computes, and pipeline the two.
+// On gfx950 the split is by wavefront inside one persistent workgroup per
+// CU that loops over (problem, 64-column group) tasks:
+//   * wave 4, the producer, streams the next task's ten lower 16 x 16 blocks
+//     of L and its 64 x 64 block of B from HBM straight into LDS with
+//     direct-to-LDS buffer loads (no registers in between; an out-of-range
+//     lane writes zeros, which gives the zero rows past m and columns past
+//     n), then inverts the next task's four diagonal blocks in place -- the
+//     inversion leaves the compute waves' critical path;
+//   * waves 0-3, the consumers, copy the current task's B from LDS into
+//     their MFMA accumulators, solve as small_mfma_kernel does (16 columns
+//     each, blocked substitution with the inverted diagonal blocks), and
+//     write X from registers;
+//   * L is double-buffered (2 x 40 KB), B single-buffered (64 KB: the
+//     consumers hold it in registers after the first moments of a task, so
+//     the producer refills it while they compute); each staged column of B
+//     has 16 bytes of padding so the consumers' column-strided LDS reads
+//     spread over the banks.  148 KB of LDS: one workgroup per CU.
+// Two barriers per task, taken by all five waves the same number of times:
+//   A(t): L(t) inverted and B(t) staged (the producer has waited for its
+//         loads and written its inversion);
+//   B(t): the consumers have copied B(t) into registers, so the B buffer is
+//         free for task t+1.
+constexpr int kPcColPitch = 64 * 16 + 16;  // bytes per staged column of B
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(320) void small_pc_kernel(int m, int64_t n, int64_t ncg, int64_t ntasks,
+                                                       Scalar alpha_s, const cplx *__restrict__ A,
+                                                       int64_t lda, int64_t strideA,
+                                                       cplx *__restrict__ B, int64_t ldb,
+                                                       int64_t strideB) {
+    using E = Elem<cplx>;
+    constexpr int TILES = 2;
+    __shared__ __attribute__((aligned(16))) cplx Ls[2][10][16][16];  // block (q,p): [k][i]
+    __shared__ __attribute__((aligned(16))) unsigned char Bs[64 * kPcColPitch];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;  // 0..3 consumers, 4 producer
+    const int np = (m + 15) >> 4;
+    // Lane indices, laundered through an empty asm at each use site: values
+    // derived from them (fragment addresses, the identity column) are cheap
+    // to recompute, and hoisted out of the task loop they would stay live
+    // across it and push the kernel past 256 VGPRs.
+    auto lane_id = [&]() {
+        int l = tid & 63;
+        asm volatile("" : "+v"(l));
+        return l;
+    };
+    const cplx alpha = E::from(alpha_s);
+    const int64_t a_ext = ((int64_t)(m - 1) * lda + m) * 16;
+    const int64_t b_ext = ((n - 1) * ldb + m) * 16;
+
+    // producer: task t's L into buffer buf, and its B
+    auto issue_loads = [&](int64_t t, int buf) {
+        const int lane = lane_id();
+        const int64_t prob = t / ncg;
+        const int64_t cg = t - prob * ncg;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + prob * strideA, a_ext);
+        const int i = lane & 15, kq = lane >> 4;
+        // rolled loops: one offset register, not one per load
+#pragma nounroll
+        for (int q = 0; q < np; ++q) {  // blocks wholly past m are never read
+#pragma nounroll
+            for (int p = 0; p <= q; ++p)
+#pragma nounroll
+                for (int kc = 0; kc < 4; ++kc) {
+                    const int gi = 16 * q + i, gk = 16 * p + 4 * kc + kq;
+                    const bool ok = gi < m && gk < m && gi >= gk;
+                    const uint32_t off = ok ? (uint32_t)((gi + (int64_t)gk * lda) * 16) : 0xfffffff0u;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void *)&Ls[buf][blk(q, p)][4 * kc][0], 16,
+                                                             off, 0, 0, 0);
+                }
+        }
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(B + prob * strideB, b_ext);
+        const int64_t cols = n - cg * 64 < 64 ? n - cg * 64 : 64;
+#pragma nounroll
+        for (int j = 0; j < cols; ++j) {
+            const int64_t col = cg * 64 + j;
+            const uint32_t off = lane < m ? (uint32_t)((lane + col * ldb) * 16) : 0xfffffff0u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)&Bs[j * kPcColPitch], 16, off, 0, 0, 0);
+        }
+    };
+    // producer: invert the diagonal blocks of buffer buf in place, lane
+    // group g taking block g, lane c column c of its inverse (section 4.3.1's
+    // substitution against identity columns); a row past m is an identity
+    // row (its loaded pivot is zero)
+    auto invert = [&](int buf) {
+        const int lane = lane_id();
+        const int c = lane & 15, g = lane >> 4;
+        if (g >= np) return;
+        cplx(*D)[16] = Ls[buf][blk(g, g)];
+        D[c][c] = (16 * g + c < m) ? E::recip(D[c][c]) : E::one();
+        cplx x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? E::one() : E::zero();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            x[k] = E::mul(x[k], D[k][k]);
+#pragma unroll
+            for (int i = k + 1; i < 16; ++i) x[i] = E::msub(x[i], D[k][i], x[k]);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) D[c][i] = x[i];
+    };
+    // vmcnt(0): the direct-to-LDS loads have written LDS
+    constexpr int kWaitVm0 = 0x0F70;
+
+    int64_t t = blockIdx.x;
+    int buf = 0;
+    if (w == 4 && t < ntasks) {
+        issue_loads(t, 0);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        invert(0);
+    }
+    __syncthreads();  // A(first task)
+    for (; t < ntasks; t += gridDim.x, buf ^= 1) {
+        const int64_t tn = t + gridDim.x;
+        d4 acc[kPanels][TILES];
+        const int lane = lane_id();
+        const int c = lane & 15, g = lane >> 4;
+        const int col_l = w * 16 + c;  // column of the task's 64 this lane solves
+        if (w < 4) {
+#pragma unroll
+            for (int p = 0; p < kPanels; ++p)
+#pragma unroll
+                for (int a = 0; a < TILES; ++a) {
+                    const int r0 = 16 * p + 8 * a + g;
+                    const cplx z0 = *reinterpret_cast<const cplx *>(&Bs[col_l * kPcColPitch + 16 * r0]);
+                    const cplx z1 = *reinterpret_cast<const cplx *>(&Bs[col_l * kPcColPitch + 16 * (r0 + 4)]);
+                    acc[p][a] = d4{z0.re, z0.im, z1.re, z1.im};
+                }
+        }
+        __syncthreads();  // B(t): the B buffer is free
+        if (w == 4) {
+            if (tn < ntasks) {
+                issue_loads(tn, buf ^ 1);
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                invert(buf ^ 1);
+            }
+        } else {
+            const cplx(*Lc)[16][16] = Ls[buf];
+#pragma unroll
+            for (int p = 0; p < kPanels; ++p) {
+                if (p < np) {  // uniform
+#pragma unroll
+                    for (int q = 0; q < p; ++q)
+#pragma unroll
+                        for (int a = 0; a < TILES; ++a)
+#pragma unroll
+                            for (int tt = 0; tt < TILES; ++tt)
+#pragma unroll
+                                for (int s = 0; s < 4; ++s)
+                                    acc[p][a] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                                        afrag(Lc[blk(p, q)], a, tt, s, c, g, -1.0), acc[q][tt][s], acc[p][a], 0, 0, 0);
+                    d4 x[TILES];
+#pragma unroll
+                    for (int a = 0; a < TILES; ++a) {
+                        x[a] = d4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+                        for (int tt = 0; tt <= a; ++tt)
+#pragma unroll
+                            for (int s = 0; s < 4; ++s)
+                                x[a] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                                    afrag(Lc[blk(p, p)], a, tt, s, c, g, 1.0), acc[p][tt][s], x[a], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int a = 0; a < TILES; ++a) acc[p][a] = x[a];
+                }
+            }
+            const int64_t prob = t / ncg;
+            const int64_t col = (t - prob * ncg) * 64 + col_l;
+            const bool colok = col < n;
+            const __amdgpu_buffer_rsrc_t rsb = make_rsrc(B + prob * strideB, b_ext);
+#pragma unroll
+            for (int p = 0; p < kPanels; ++p)
+#pragma unroll
+                for (int a = 0; a < TILES; ++a) {
+                    const int r0 = 16 * p + 8 * a + g;
+                    st_elem<cplx>(rsb, r0 + col * ldb, colok && r0 < m, E::mul(alpha, cplx{acc[p][a][0], acc[p][a][1]}));
+                    st_elem<cplx>(rsb, r0 + 4 + col * ldb, colok && r0 + 4 < m,
+                                  E::mul(alpha, cplx{acc[p][a][2], acc[p][a][3]}));
+                }
+        }
+        __syncthreads();  // A(t + gridDim.x)
+    }
+}
+
+int device_cus() {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = cus;
+    return cus;
+}
+
+// Producer/consumer form for complex fp64: opt-in (TRSM_SMALL_PC=1), for
+// tuning and tests.  Measured on MI355X for a batch of 8192 complex 64 x 64
+// problems it ran 466 us against 280 us for small_mfma_kernel: with 148 KB
+// of LDS one workgroup fits a CU, so one producer wave per CU keeps too few
+// loads in flight (its side alone, with the consumers' products skipped,
+// took 342 us) and one MFMA wave per SIMD leaves the products' LDS and
+// dependency latencies exposed (the consumers' side alone, 359 us); three
+// resident workgroup-per-task workgroups per CU hide both.
+bool use_small_pc(int64_t ntasks, int cus) {
+    (void)ntasks;
+    (void)cus;
+    const char *e = std::getenv("TRSM_SMALL_PC");
+    return e && e[0] == '1';
+}
+
 }  // namespace
 
 hipError_t small_mfma_launch(int dtype, int m, int64_t n, Scalar alpha, const void *A,
@@ -325,9 +550,18 @@ hipError_t small_mfma_launch(int dtype, int m, int64_t n, Scalar alpha, const vo
                                    static_cast<const double *>(A), lda, strideA, static_cast<double *>(B), ldb, strideB);
             break;
         case C64F:
-            if (buf)
+            if (buf) {
+                const int cus = device_cus();
+                if (cus > 0 && use_small_pc(nblk, cus)) {
+                    const int64_t nwg = nblk < cus ? nblk : cus;
+                    hipLaunchKernelGGL(small_pc_kernel, dim3((unsigned)nwg), dim3(320), 0, stream, m, n, ncg, nblk,
+                                       alpha, static_cast<const cplx *>(A), lda, strideA, static_cast<cplx *>(B),
+                                       ldb, strideB);
+                    break;
+                }
                 hipLaunchKernelGGL((small_mfma_kernel<cplx, true>), grid, dim3(256), 0, stream, m, n, ncg, alpha,
                                    static_cast<const cplx *>(A), lda, strideA, static_cast<cplx *>(B), ldb, strideB);
+            }
             else
                 hipLaunchKernelGGL((small_mfma_kernel<cplx, false>), grid, dim3(256), 0, stream, m, n, ncg, alpha,
                                    static_cast<const cplx *>(A), lda, strideA, static_cast<cplx *>(B), ldb, strideB);
