@@ -46,14 +46,17 @@ def rand(dtype, rows, cols, rng, ld=None):
     return base.T[:rows]
 
 
-def gemm_case(T, dtype, M, N, K, beta, gamma, *, seed=0, ldpad=0, split=0, a_lower=False):
+def gemm_case(T, dtype, M, N, K, beta, gamma, *, seed=0, ldpad=0, split=0, a_lower=False,
+              ldpad_a=None, ldpad_b=None):
     import torch
     rng = np.random.default_rng(seed)
-    A = rand(dtype, M, K, rng, M + ldpad)
+    pa = ldpad if ldpad_a is None else ldpad_a
+    pb = ldpad if ldpad_b is None else ldpad_b
+    A = rand(dtype, M, K, rng, M + pa)
     if a_lower:
         A = np.asfortranarray(np.tril(A))
-        A = rand_like_ld(A, M + ldpad)
-    Bm = rand(dtype, K, N, rng, K + ldpad)
+        A = rand_like_ld(A, M + pa)
+    Bm = rand(dtype, K, N, rng, K + pb)
     C = rand(dtype, M, N, rng, M + ldpad)
     Ad, Bd, Cd = to_dev(A), to_dev(Bm), to_dev(C)
     Dd = to_dev(np.full((M, N), np.nan, dtype=NP[dtype], order="F"), ld=M + ldpad)
@@ -113,6 +116,41 @@ def test_gemm_fp64_128x128_tile(T):
     and 1."""
     gemm_case(T, "f64", 2000, 4000, 46, 1.0, -1.0, seed=5)
     gemm_case(T, "f64", 2000, 4000, 302, 0.0, 0.5, seed=6)
+
+
+LF_CASES = [
+    # (M, N, K, ldpad, split, beta, gamma): 16 x 32 = 512 tiles of 128 x 128,
+    # 16-byte aligned operands (even leading dimensions)
+    (2000, 4000, 0, 0, 0, 1.5, -1.0),      # K = 0: D = beta C
+    (2000, 4000, 1, 1, 0, 1.0, -1.0),      # a single k
+    (2000, 4000, 7, 1, 0, 0.0, 0.5),
+    (2000, 4000, 8, 0, 0, 1.0, -1.0),      # one full chunk
+    (2000, 4000, 9, 1, 0, 1.0, -1.0),
+    (2000, 4000, 23, 1, 0, -0.5, 2.0),
+    (2000, 4000, 46, 2, 0, 1.0, -1.0),     # NaN in the rows of Bm past K
+    (1999, 4000, 63, 1, 0, 1.0, -1.0),     # odd M: a row pair split at the edge
+    (2000, 4000, 64, 0, 100, 1.0, -1.0),   # rows below 100 routed to D2
+    (2000, 4000, 1001, 1, 37, 0.5, -1.0),  # odd split
+    (2000, 3999, 128, 0, 0, 1.0, -1.0),    # ragged N
+]
+
+
+@pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("case", LF_CASES)
+def test_gemm_fp64_lds_free_edges(T, case, lf, monkeypatch):
+    """fp64 products on the 128 x 128 tile run the LDS-free kernel (each wave
+    streams its own operands into a register ring; TRSM_GEMM_LF=0 runs the
+    LDS-staged tile instead, so both are checked): every K modulo the 8-wide
+    chunk, K = 0, NaN stored right past K in Bm (the ragged chunk must read
+    zeros there), odd M, ragged N, the D2 split (even and odd) and several
+    beta / gamma."""
+    monkeypatch.setenv("TRSM_GEMM_LF", lf)
+    M, N, K, ldpad, split, beta, gamma = case
+    # even leading dimensions of A and Bm: 16-byte aligned columns
+    pa = ldpad + (M + ldpad) % 2
+    pb = ldpad + (K + ldpad) % 2
+    gemm_case(T, "f64", M, N, K, beta, gamma, seed=K + M, ldpad=ldpad, ldpad_a=pa, ldpad_b=pb,
+              split=split)
 
 
 @pytest.mark.parametrize("dtype", ["f64", "c64"])

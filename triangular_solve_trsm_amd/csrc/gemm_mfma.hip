@@ -55,6 +55,7 @@
 //   * a product with few output tiles and a long K (a narrow B) can be cut
 //     along K (gemm_splitk_launch): the chunks run as one batched launch
 //     into partial sums, which a reduction kernel adds in a fixed order.
+#include <cstdlib>
 #include <type_traits>
 
 #include "buffer_ops.h"
@@ -66,6 +67,7 @@ namespace {
 typedef double d4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef double d2v __attribute__((ext_vector_type(2)));
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
 template <typename T> struct GemmTraits;
 template <> struct GemmTraits<float> {
     using R = float;
@@ -587,6 +589,184 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
     }  // pass
 }
 
+// ---- fp64 products without LDS ---------------------------------------------
+// A v_mfma_f64_16x16x4f64 holds the matrix core of its SIMD for 64 cycles, so
+// on gfx950 the fp64 operands are cheap next to the arithmetic, and the
+// shared-LDS pipeline of gemm_kernel loses its time at the K-tile boundaries
+// (the wait for the next tile, the LDS hand-off, the barrier), with two
+// waves per SIMD to hide it.  gemm_lf_kernel has neither LDS nor barriers:
+// each wave computes 64 x 64 outputs of its workgroup's 128 x 128 tile and
+// streams its own rows of A and columns of Bm from memory (mostly L2) into a
+// ring of registers, RING chunks of 8 k ahead of the products that use them.
+//   * A: lane (c, q) (c = lane % 16, q = lane / 16) loads rows 2c, 2c + 1
+//     and 32 + 2c, 33 + 2c of the wave's 64 at chunk k = 2q + s (s = 0, 1),
+//     16 bytes each, consecutive lanes on consecutive rows; MFMA row tile a
+//     takes row 2c + (a & 1) + 32 (a >> 1) as its row c;
+//   * Bm: lane (c, q) loads k = 2q, 2q + 1 of columns c + 16b (b = 0..3),
+//     16 bytes each; k index q of MFMA step s is chunk k 2q + s on both
+//     sides (the order of a sum over k is free);
+//   * the f64 result puts MFMA row q + 4v in item v of lane group q, so a
+//     lane holds output rows 2(q + 4v), 2(q + 4v) + 1 (tiles 0, 1) and 32
+//     rows further (tiles 2, 3): C and D move in 16-byte pairs;
+//   * loads are raw buffer loads rebased per chunk: a read past the end of
+//     an operand returns zero, and the ragged last chunk (K % 8) gives the
+//     lanes whose k is past K an offset out of range, so A and Bm both read
+//     zero there (whatever the memory past K holds).
+// Measured on MI355X against the 128 x 128 gemm_kernel tile, fp64
+// 1024 x 8192 updates: 68.3 against 64.5 TFLOP/s at K = 7168, 67.7 against
+// 63.9 at K = 4096, 64.9 against 59.3 at K = 1024.
+template <int RING>
+__global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    // wave-uniform (the buffer resources below are built from it and must
+    // be scalar values)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15;
+    const int q = lane >> 4;
+    int tm, tn;
+    map_tile(blockIdx.x, p.tilesM, p.tilesN, tm, tn);
+    const int64_t r0 = (int64_t)tm * 128 + (wave & 1) * 64;  // the wave's first row
+    const int64_t c0 = (int64_t)tn * 128 + (wave >> 1) * 64;  // and first column
+    const double *__restrict__ pA = p.A;
+    const double *__restrict__ pB = p.Bm;
+    const int64_t lda = p.lda, ldb = p.ldb;
+
+    // ---- accumulators start at sc * C ----------------------------------------
+    d4 acc[4][4];
+    const double sc = p.sc.re;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int64_t j = c0 + c16 + 16 * b;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t rr = r0 + 2 * (q + 4 * v);
+            double x[4] = {0.0, 0.0, 0.0, 0.0};
+            if (p.has_c && j < p.N) {
+                const double *col = p.C + j * p.ldc;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {  // rows rr (tiles 0, 1) and rr + 32 (tiles 2, 3)
+                    const int64_t r = rr + 32 * h;
+                    if (p.c_vec && r + 1 < p.M) {
+                        const d2v c2 = *reinterpret_cast<const d2v *>(col + r);
+                        x[2 * h] = c2[0];
+                        x[2 * h + 1] = c2[1];
+                    } else {
+                        if (r < p.M) x[2 * h] = col[r];
+                        if (r + 1 < p.M) x[2 * h + 1] = col[r + 1];
+                    }
+                }
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a) acc[a][b][v] = sc * x[a];
+        }
+    }
+
+    // ---- operand ring -------------------------------------------------------
+    const uint32_t offA0 = (uint32_t)((2 * c16 + 2 * q * lda) * 8);
+    const uint32_t offA1 = offA0 + (uint32_t)(lda * 8);
+    uint32_t offB[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) offB[b] = (uint32_t)((2 * q + (c16 + 16 * (int64_t)b) * ldb) * 8);
+    d2v ra[RING][4], rb[RING][4];
+    // chunk [k0, k0 + 8) into ring slot `slot`; live == false issues loads
+    // on an empty range (no memory access, zeros)
+    auto load = [&](int slot, int64_t k0, bool live) {
+        const int64_t oa = r0 + k0 * lda;
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, live ? (p.extA - oa) * 8 : 0);
+        ra[slot][0] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0));
+        ra[slot][1] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0 + 256));
+        ra[slot][2] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1));
+        ra[slot][3] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1 + 256));
+        const int64_t ob = k0 + c0 * ldb;
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, live ? (p.extB - ob) * 8 : 0);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) rb[slot][b] = __builtin_bit_cast(d2v, ld16<true>(rsb, offB[b]));
+    };
+    auto compute = [&](const d2v (&a4)[4], const d2v (&b4)[4]) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const double av[4] = {a4[2 * s][0], a4[2 * s][1], a4[2 * s + 1][0], a4[2 * s + 1][1]};
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], b4[b][s], acc[a][b], 0, 0, 0);
+        }
+    };
+    const int64_t nkf = p.K / 8;  // full chunks
+#pragma unroll
+    for (int u = 0; u < RING; ++u) load(u, 8 * u, u < nkf);
+    for (int64_t kc = 0; kc < nkf; kc += RING) {
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+            if (kc + u < nkf) {  // uniform
+                compute(ra[u], rb[u]);
+                load(u, 8 * (kc + u + RING), kc + u + RING < nkf);
+            }
+        }
+    }
+    // ragged last chunk: k = 8 nkf + 2q + s exists only while below K; the
+    // lanes past it read zero from A and Bm (8-byte Bm loads, so a pair
+    // straddling K keeps its first element)
+    const int kr = (int)(p.K - 8 * nkf);
+    if (kr > 0) {
+        const int64_t k0 = 8 * nkf;
+        const int64_t oa = r0 + k0 * lda;
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, (p.extA - oa) * 8);
+        const uint32_t dead = 0xfffffff0u;
+        const bool ok0 = 2 * q < kr, ok1 = 2 * q + 1 < kr;
+        d2v ta[4], tb[4];
+        ta[0] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok0 ? offA0 : dead));
+        ta[1] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok0 ? offA0 + 256 : dead));
+        ta[2] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 : dead));
+        ta[3] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 + 256 : dead));
+        const int64_t ob = k0 + c0 * ldb;
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, (p.extB - ob) * 8);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const u2v lo = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok0 ? offB[b] : dead, 0, 0);
+            const u2v hi = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok1 ? offB[b] + 8 : dead, 0, 0);
+            tb[b] = d2v{__builtin_bit_cast(double, lo), __builtin_bit_cast(double, hi)};
+        }
+        compute(ta, tb);
+    }
+
+    // ---- epilogue: D = gamma * acc, rows below `split` to D2 ------------------
+    const double gamma = p.gamma.re;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int64_t j = c0 + c16 + 16 * b;
+        if (j >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t r = r0 + 2 * (q + 4 * v) + 32 * h;
+                if (r >= p.M) continue;
+                const double x0 = gamma * acc[2 * h][b][v];
+                const double x1 = gamma * acc[2 * h + 1][b][v];
+                if (r + 1 < p.M && r + 1 < p.split) {
+                    double *dst = p.D2 + j * p.ldd2 + r;
+                    if (p.d2_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
+                    else { dst[0] = x0; dst[1] = x1; }
+                } else if (r + 1 < p.M && r >= p.split) {
+                    double *dst = p.D + j * p.ldd + r;
+                    if (p.d_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
+                    else { dst[0] = x0; dst[1] = x1; }
+                } else {
+                    if (r < p.split) p.D2[r + j * p.ldd2] = x0;
+                    else p.D[r + j * p.ldd] = x0;
+                    if (r + 1 < p.M) {
+                        if (r + 1 < p.split) p.D2[r + 1 + j * p.ldd2] = x1;
+                        else p.D[r + 1 + j * p.ldd] = x1;
+                    }
+                }
+            }
+        }
+    }
+}
+
 inline bool aligned16(const void *ptr, int64_t ld, size_t es) {
     return (reinterpret_cast<uintptr_t>(ptr) % 16) == 0 && ((int64_t)es * ld) % 16 == 0;
 }
@@ -707,6 +887,22 @@ hipError_t launch_wide(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// fp64 single products on gemm_lf_kernel (TRSM_GEMM_LF=0 turns it off for
+// tuning and tests).
+bool use_gemm_lf() {
+    const char *e = std::getenv("TRSM_GEMM_LF");
+    return !(e && e[0] == '0');
+}
+
+hipError_t launch_lf(const GemmDesc &g, hipStream_t st) {
+    GemmParams<double> p;
+    dim3 grid;
+    hipError_t e = tile_params<double, 128, 128>(g, p, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    hipLaunchKernelGGL((gemm_lf_kernel<3>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
 // Macro tile, from timings on MI355X of the update and solve sequences of
 // blocked solves (fp32 4096^2, fp64 1024^2 .. 8192^2, complex 8192 x 2048):
 //   * 64 x 32 for the triangular solve products (each workgroup folds two
@@ -767,8 +963,12 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
             // ran 41.5 TFLOP/s where 64 x 64 tiles fill their rounds.
             const int64_t t128 = ((Mr + 127) / 128) * ((g.N + 127) / 128);
             if (Mr > 64 && t128 >= 512 && 4 * t128 >= 3 * 512 * ((t128 + 511) / 512) &&
-                aligned16(g.A, g.lda, sizeof(T)) && aligned16(g.Bm, g.ldb, sizeof(T)))
+                aligned16(g.A, g.lda, sizeof(T)) && aligned16(g.Bm, g.ldb, sizeof(T))) {
+                if constexpr (std::is_same<T, double>::value) {
+                    if (use_gemm_lf()) return launch_lf(g, st);
+                }
                 return launch_tile<T, 128, 128, KT>(g, st);
+            }
             if (((Mr + 127) / 128) * ((g.N + 63) / 64) >= 2048) return launch_tile<T, 128, 64, KT>(g, st);
         }
         if (((Mr + 63) / 64) * ((g.N + 63) / 64) < 1024) return launch_tile<T, 64, 32, KT>(g, st);
