@@ -153,6 +153,20 @@ def test_gemm_fp64_lds_free_edges(T, case, lf, monkeypatch):
               split=split)
 
 
+@pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("M,N", [(1000, 8100), (960, 8192), (1023, 8192), (1024, 8190)])
+def test_gemm_fp64_lds_free_triangular(T, M, N, lf, monkeypatch):
+    """Triangular fp64 products with at least 512 workgroups run the LDS-free
+    form (TRSM_GEMM_LF=0: the LDS tile): each wave takes the 64-row tiles i
+    and T-1-i of a 32-column block, each over K up to its own diagonal.
+    Ragged last row tile (1000 = 15 x 64 + 40), an odd count of row tiles
+    (960: the middle tile runs alone), odd M (a row pair split at the edge),
+    ragged N."""
+    monkeypatch.setenv("TRSM_GEMM_LF", lf)
+    pa = M % 2  # even leading dimensions: 16-byte aligned columns
+    gemm_case(T, "f64", M, N, M, 0.0, -0.75, seed=M + N, a_lower=True, ldpad_a=pa, ldpad_b=pa)
+
+
 @pytest.mark.parametrize("dtype", ["f64", "c64"])
 def test_gemm_triangular_wide_tiles(T, dtype):
     """Triangular products with 512 folded workgroups on the wider tile

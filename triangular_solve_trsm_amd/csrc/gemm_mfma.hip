@@ -615,7 +615,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
 // Measured on MI355X against the 128 x 128 gemm_kernel tile, fp64
 // 1024 x 8192 updates: 68.3 against 64.5 TFLOP/s at K = 7168, 67.7 against
 // 63.9 at K = 4096, 64.9 against 59.3 at K = 1024.
-template <int RING>
+// NBT: 16-column MFMA tiles per wave (4: 64 x 64 per wave, the workgroup a
+// 2 x 2 grid of waves on 128 x 128; 2: 64 x 32 per wave, the workgroup four
+// waves side by side on 64 x 128).
+// TRI: A is lower triangular with explicit zeros above the diagonal (the
+// diagonal-block solve, M == K): a 64-row tile at r0 needs K up to r0 + 64
+// only; each wave takes row tiles i and T-1-i (T = 64-row tiles) one after
+// the other, so every wave gets the same length of K (no barriers: waves
+// run independently).
+template <int RING, int NBT, bool TRI>
 __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -626,144 +634,160 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
     const int q = lane >> 4;
     int tm, tn;
     map_tile(blockIdx.x, p.tilesM, p.tilesN, tm, tn);
-    const int64_t r0 = (int64_t)tm * 128 + (wave & 1) * 64;  // the wave's first row
-    const int64_t c0 = (int64_t)tn * 128 + (wave >> 1) * 64;  // and first column
     const double *__restrict__ pA = p.A;
     const double *__restrict__ pB = p.Bm;
     const int64_t lda = p.lda, ldb = p.ldb;
-
-    // ---- accumulators start at sc * C ----------------------------------------
-    d4 acc[4][4];
-    const double sc = p.sc.re;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int64_t j = c0 + c16 + 16 * b;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t rr = r0 + 2 * (q + 4 * v);
-            double x[4] = {0.0, 0.0, 0.0, 0.0};
-            if (p.has_c && j < p.N) {
-                const double *col = p.C + j * p.ldc;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {  // rows rr (tiles 0, 1) and rr + 32 (tiles 2, 3)
-                    const int64_t r = rr + 32 * h;
-                    if (p.c_vec && r + 1 < p.M) {
-                        const d2v c2 = *reinterpret_cast<const d2v *>(col + r);
-                        x[2 * h] = c2[0];
-                        x[2 * h + 1] = c2[1];
-                    } else {
-                        if (r < p.M) x[2 * h] = col[r];
-                        if (r + 1 < p.M) x[2 * h + 1] = col[r + 1];
-                    }
-                }
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a) acc[a][b][v] = sc * x[a];
-        }
-    }
-
-    // ---- operand ring -------------------------------------------------------
     const uint32_t offA0 = (uint32_t)((2 * c16 + 2 * q * lda) * 8);
     const uint32_t offA1 = offA0 + (uint32_t)(lda * 8);
-    uint32_t offB[4];
+    uint32_t offB[NBT];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) offB[b] = (uint32_t)((2 * q + (c16 + 16 * (int64_t)b) * ldb) * 8);
-    d2v ra[RING][4], rb[RING][4];
-    // chunk [k0, k0 + 8) into ring slot `slot`; live == false issues loads
-    // on an empty range (no memory access, zeros)
-    auto load = [&](int slot, int64_t k0, bool live) {
-        const int64_t oa = r0 + k0 * lda;
-        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, live ? (p.extA - oa) * 8 : 0);
-        ra[slot][0] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0));
-        ra[slot][1] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0 + 256));
-        ra[slot][2] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1));
-        ra[slot][3] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1 + 256));
-        const int64_t ob = k0 + c0 * ldb;
-        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, live ? (p.extB - ob) * 8 : 0);
+    for (int b = 0; b < NBT; ++b) offB[b] = (uint32_t)((2 * q + (c16 + 16 * (int64_t)b) * ldb) * 8);
+    const double sc = p.sc.re, gamma = p.gamma.re;
+
+    // the wave's output block: rows [r0, r0 + 64), columns [c0, c0 + 16 NBT),
+    // products over k in [0, K)
+    auto run_tile = [&](const int64_t r0, const int64_t c0, const int64_t K) {
+        // ---- accumulators start at sc * C ------------------------------------
+        d4 acc[4][NBT];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) rb[slot][b] = __builtin_bit_cast(d2v, ld16<true>(rsb, offB[b]));
-    };
-    auto compute = [&](const d2v (&a4)[4], const d2v (&b4)[4]) {
+        for (int b = 0; b < NBT; ++b) {
+            const int64_t j = c0 + c16 + 16 * b;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const double av[4] = {a4[2 * s][0], a4[2 * s][1], a4[2 * s + 1][0], a4[2 * s + 1][1]};
+            for (int v = 0; v < 4; ++v) {
+                const int64_t rr = r0 + 2 * (q + 4 * v);
+                double x[4] = {0.0, 0.0, 0.0, 0.0};
+                if (p.has_c && j < p.N) {
+                    const double *col = p.C + j * p.ldc;
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+                    for (int h = 0; h < 2; ++h) {  // rows rr (tiles 0, 1) and rr + 32 (tiles 2, 3)
+                        const int64_t r = rr + 32 * h;
+                        if (p.c_vec && r + 1 < p.M) {
+                            const d2v c2 = *reinterpret_cast<const d2v *>(col + r);
+                            x[2 * h] = c2[0];
+                            x[2 * h + 1] = c2[1];
+                        } else {
+                            if (r < p.M) x[2 * h] = col[r];
+                            if (r + 1 < p.M) x[2 * h + 1] = col[r + 1];
+                        }
+                    }
+                }
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], b4[b][s], acc[a][b], 0, 0, 0);
-        }
-    };
-    const int64_t nkf = p.K / 8;  // full chunks
-#pragma unroll
-    for (int u = 0; u < RING; ++u) load(u, 8 * u, u < nkf);
-    for (int64_t kc = 0; kc < nkf; kc += RING) {
-#pragma unroll
-        for (int u = 0; u < RING; ++u) {
-            if (kc + u < nkf) {  // uniform
-                compute(ra[u], rb[u]);
-                load(u, 8 * (kc + u + RING), kc + u + RING < nkf);
+                for (int a = 0; a < 4; ++a) acc[a][b][v] = sc * x[a];
             }
         }
-    }
-    // ragged last chunk: k = 8 nkf + 2q + s exists only while below K; the
-    // lanes past it read zero from A and Bm (8-byte Bm loads, so a pair
-    // straddling K keeps its first element)
-    const int kr = (int)(p.K - 8 * nkf);
-    if (kr > 0) {
-        const int64_t k0 = 8 * nkf;
-        const int64_t oa = r0 + k0 * lda;
-        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, (p.extA - oa) * 8);
-        const uint32_t dead = 0xfffffff0u;
-        const bool ok0 = 2 * q < kr, ok1 = 2 * q + 1 < kr;
-        d2v ta[4], tb[4];
-        ta[0] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok0 ? offA0 : dead));
-        ta[1] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok0 ? offA0 + 256 : dead));
-        ta[2] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 : dead));
-        ta[3] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 + 256 : dead));
-        const int64_t ob = k0 + c0 * ldb;
-        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, (p.extB - ob) * 8);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const u2v lo = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok0 ? offB[b] : dead, 0, 0);
-            const u2v hi = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok1 ? offB[b] + 8 : dead, 0, 0);
-            tb[b] = d2v{__builtin_bit_cast(double, lo), __builtin_bit_cast(double, hi)};
-        }
-        compute(ta, tb);
-    }
 
-    // ---- epilogue: D = gamma * acc, rows below `split` to D2 ------------------
-    const double gamma = p.gamma.re;
+        // ---- operand ring -----------------------------------------------------
+        d2v ra[RING][4], rb[RING][NBT];
+        // chunk [k0, k0 + 8) into ring slot `slot`; live == false issues the
+        // loads on an empty range (no memory access, zeros)
+        auto load = [&](int slot, int64_t k0, bool live) {
+            const int64_t oa = r0 + k0 * lda;
+            const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, live ? (p.extA - oa) * 8 : 0);
+            ra[slot][0] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0));
+            ra[slot][1] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0 + 256));
+            ra[slot][2] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1));
+            ra[slot][3] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1 + 256));
+            const int64_t ob = k0 + c0 * ldb;
+            const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, live ? (p.extB - ob) * 8 : 0);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int64_t j = c0 + c16 + 16 * b;
-        if (j >= p.N) continue;
+            for (int b = 0; b < NBT; ++b) rb[slot][b] = __builtin_bit_cast(d2v, ld16<true>(rsb, offB[b]));
+        };
+        auto compute = [&](const d2v (&a4)[4], const d2v (&bq)[NBT]) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+            for (int s = 0; s < 2; ++s) {
+                const double av[4] = {a4[2 * s][0], a4[2 * s][1], a4[2 * s + 1][0], a4[2 * s + 1][1]};
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int64_t r = r0 + 2 * (q + 4 * v) + 32 * h;
-                if (r >= p.M) continue;
-                const double x0 = gamma * acc[2 * h][b][v];
-                const double x1 = gamma * acc[2 * h + 1][b][v];
-                if (r + 1 < p.M && r + 1 < p.split) {
-                    double *dst = p.D2 + j * p.ldd2 + r;
-                    if (p.d2_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
-                    else { dst[0] = x0; dst[1] = x1; }
-                } else if (r + 1 < p.M && r >= p.split) {
-                    double *dst = p.D + j * p.ldd + r;
-                    if (p.d_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
-                    else { dst[0] = x0; dst[1] = x1; }
-                } else {
-                    if (r < p.split) p.D2[r + j * p.ldd2] = x0;
-                    else p.D[r + j * p.ldd] = x0;
-                    if (r + 1 < p.M) {
-                        if (r + 1 < p.split) p.D2[r + 1 + j * p.ldd2] = x1;
-                        else p.D[r + 1 + j * p.ldd] = x1;
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < NBT; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bq[b][s], acc[a][b], 0, 0, 0);
+            }
+        };
+        const int64_t nkf = K / 8;  // full chunks
+#pragma unroll
+        for (int u = 0; u < RING; ++u) load(u, 8 * u, u < nkf);
+        for (int64_t kc = 0; kc < nkf; kc += RING) {
+#pragma unroll
+            for (int u = 0; u < RING; ++u) {
+                if (kc + u < nkf) {  // uniform
+                    compute(ra[u], rb[u]);
+                    load(u, 8 * (kc + u + RING), kc + u + RING < nkf);
+                }
+            }
+        }
+        // ragged last chunk: k = 8 nkf + 2q + s exists only while below K; the
+        // lanes past it read zero from A and Bm (8-byte Bm loads, so a pair
+        // straddling K keeps its first element)
+        const int kr = (int)(K - 8 * nkf);
+        if (kr > 0) {
+            const int64_t k0 = 8 * nkf;
+            const int64_t oa = r0 + k0 * lda;
+            const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, (p.extA - oa) * 8);
+            const uint32_t dead = 0xfffffff0u;
+            const bool ok0 = 2 * q < kr, ok1 = 2 * q + 1 < kr;
+            d2v ta[4], tb[NBT];
+            ta[0] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok0 ? offA0 : dead));
+            ta[1] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok0 ? offA0 + 256 : dead));
+            ta[2] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 : dead));
+            ta[3] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 + 256 : dead));
+            const int64_t ob = k0 + c0 * ldb;
+            const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, (p.extB - ob) * 8);
+#pragma unroll
+            for (int b = 0; b < NBT; ++b) {
+                const u2v lo = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok0 ? offB[b] : dead, 0, 0);
+                const u2v hi = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok1 ? offB[b] + 8 : dead, 0, 0);
+                tb[b] = d2v{__builtin_bit_cast(double, lo), __builtin_bit_cast(double, hi)};
+            }
+            compute(ta, tb);
+        }
+
+        // ---- epilogue: D = gamma * acc, rows below `split` to D2 ----------------
+#pragma unroll
+        for (int b = 0; b < NBT; ++b) {
+            const int64_t j = c0 + c16 + 16 * b;
+            if (j >= p.N) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t r = r0 + 2 * (q + 4 * v) + 32 * h;
+                    if (r >= p.M) continue;
+                    const double x0 = gamma * acc[2 * h][b][v];
+                    const double x1 = gamma * acc[2 * h + 1][b][v];
+                    if (r + 1 < p.M && r + 1 < p.split) {
+                        double *dst = p.D2 + j * p.ldd2 + r;
+                        if (p.d2_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
+                        else { dst[0] = x0; dst[1] = x1; }
+                    } else if (r + 1 < p.M && r >= p.split) {
+                        double *dst = p.D + j * p.ldd + r;
+                        if (p.d_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
+                        else { dst[0] = x0; dst[1] = x1; }
+                    } else {
+                        if (r < p.split) p.D2[r + j * p.ldd2] = x0;
+                        else p.D[r + j * p.ldd] = x0;
+                        if (r + 1 < p.M) {
+                            if (r + 1 < p.split) p.D2[r + 1 + j * p.ldd2] = x1;
+                            else p.D[r + 1 + j * p.ldd] = x1;
+                        }
                     }
                 }
             }
         }
+    };
+
+    if constexpr (TRI) {
+        // tm: pair of 64-row tiles (tm, T-1-tm); the wave's 16 NBT columns
+        const int T = (int)((p.M + 63) / 64);
+        const int64_t c0 = (int64_t)tn * 64 * NBT + (int64_t)wave * 16 * NBT;
+        const int t1 = T - 1 - tm;
+        for (int pass = 0; pass < (t1 != tm ? 2 : 1); ++pass) {
+            const int64_t r0 = (int64_t)(pass == 0 ? tm : t1) * 64;
+            run_tile(r0, c0, r0 + 64 < p.K ? r0 + 64 : p.K);
+        }
+    } else {
+        const int64_t r0 = (int64_t)tm * 128 + (wave & 1) * 64;
+        const int64_t c0 = (int64_t)tn * 32 * NBT + (int64_t)(wave >> 1) * 16 * NBT;
+        run_tile(r0, c0, p.K);
     }
 }
 
@@ -899,7 +923,26 @@ hipError_t launch_lf(const GemmDesc &g, hipStream_t st) {
     dim3 grid;
     hipError_t e = tile_params<double, 128, 128>(g, p, grid);
     if (e != hipSuccess || grid.x == 0) return e;
-    hipLaunchKernelGGL((gemm_lf_kernel<3>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_lf_kernel<3, 4, false>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+// Triangular fp64 product (the diagonal-block solve): workgroups of four
+// 64 x 32 waves over 128 columns, each wave on the row-tile pair (i, T-1-i),
+// with a ring of five chunks.  Measured on the 1024 x 8192 solve of fp64
+// 8192^2: 168 us with the 64 x 32 wave tile and a ring of 3, 162 with 4,
+// 158 with 5; a 64 x 64 wave tile (one wave per SIMD) 178 us; the LDS tile
+// (64 x 128) 171 us.
+hipError_t launch_lf_tri(const GemmDesc &g, hipStream_t st) {
+    GemmParams<double> p;
+    dim3 grid;
+    hipError_t e = tile_params<double, 64, 128>(g, p, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    const int64_t T = (g.M + 63) / 64;
+    p.tilesM = (int)((T + 1) / 2);  // row-tile pairs
+    p.tilesN = (int)((g.N + 127) / 128);
+    grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
+    hipLaunchKernelGGL((gemm_lf_kernel<5, 2, true>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -943,7 +986,11 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
         const int64_t pairs = ((Mr + 63) / 64 + 1) / 2;
         if constexpr (std::is_same<T, double>::value) {
-            if (pairs * ((g.N + 127) / 128) >= 512) return launch_tile<T, 64, 128, KT>(g, st);
+            if (pairs * ((g.N + 127) / 128) >= 512) {
+                if (use_gemm_lf() && aligned16(g.A, g.lda, 8) && aligned16(g.Bm, g.ldb, 8))
+                    return launch_lf_tri(g, st);
+                return launch_tile<T, 64, 128, KT>(g, st);
+            }
         }
         if constexpr (std::is_same<T, cplx>::value) {
             if (pairs * ((g.N + 63) / 64) >= 512) return launch_tile<T, 64, 64, KT>(g, st);
