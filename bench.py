@@ -214,7 +214,6 @@ def protocol_time(T, call, restore, warm_s=0.3, runs=9):
     call()  # the protocol's own warm-up run
     torch.cuda.synchronize()
     ts = []
-    T.trsm_profile_start()
     for _ in range(runs):
         restore()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -223,6 +222,15 @@ def protocol_time(T, call, restore, warm_s=0.3, runs=9):
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
+    # per-launch records from separate runs: two event records around each
+    # of a solve's launches lengthen a short solve measurably (fp32 4096^2,
+    # 17 launches: 0.71 -> 0.78 ms), so the timed runs above take none
+    T.trsm_profile_select(None)
+    T.trsm_profile_start()
+    for _ in range(3):
+        restore()
+        call()
+    torch.cuda.synchronize()
     T.trsm_profile_stop()
     return sum(ts) / len(ts), min(ts), T.profile_records()
 
@@ -253,7 +261,7 @@ def time_other_configs(T, to_dev_fn, a4d, b4_host, a4, cfg4):
         if cfg.m > 64:
             e["phases"] = phase_split(recs)
             kern = summarize_kernels(recs)
-            e["kernels"] = {k: {"mean_ms": v["mean_ms"], "launches_per_solve": v["launches"] / 9,
+            e["kernels"] = {k: {"mean_ms": v["mean_ms"], "launches_per_solve": v["launches"] / 3,
                                 "tflops": v["tflops"]} for k, v in kern.items()}
         e.update(extra)
         return e
@@ -265,7 +273,11 @@ def time_other_configs(T, to_dev_fn, a4d, b4_host, a4, cfg4):
         Ad, B0 = to_dev_fn(L), to_dev_fn(B)
         Bd = B0.clone()
         del L, B
-        mean_ms, min_ms, recs = protocol_time(T, lambda: T.trsm_lln(Ad, Bd, a), lambda: Bd.copy_(B0))
+        # one second of the same call first: the clock drops while the host
+        # draws the inputs, and 0.3 s did not bring it back (C3 read 0.78 ms
+        # where it runs 0.71 ms in steady state)
+        mean_ms, min_ms, recs = protocol_time(T, lambda: T.trsm_lln(Ad, Bd, a), lambda: Bd.copy_(B0),
+                                              warm_s=1.0)
         extra = {}
         if cfg.m > 64:
             extra["ib"] = T.trsm_lln_select_ib({"f32": T.R32F, "f64": T.R64F, "c64": T.C64F}[cfg.dtype],
@@ -379,12 +391,22 @@ def main():
     A2d, B2d = to_dev(L2), to_dev(B2)
     torch.cuda.synchronize()
 
-    def step():
+    marks = []  # (event before C4, between, after C2) per timed step
+
+    def step(mark=False):
+        if mark:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
         if args.ib:
             T.trsm_lln_ex(A4d, B4d, a4, ib=args.ib)
         else:
             T.trsm_lln(A4d, B4d, a4)
+        if mark:
+            ev[1].record()
         T.trsm_lln_strided_batched(A2d, B2d, a2)
+        if mark:
+            ev[2].record()
+            marks.append(ev)
 
     parity = None
     if not args.no_check:
@@ -422,12 +444,16 @@ def main():
 
     log(f"timing {args.steps} steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # HIP events around the dominant kernel's launches (and the batched small
+    # solve's, for its HBM figure) only: events around every launch would
+    # lengthen the step they measure
+    T.trsm_profile_select(["update_gemm", "small"])
     T.trsm_profile_start()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(args.steps):
-        step()
+        step(mark=True)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -441,9 +467,8 @@ def main():
     value = flops_step * args.steps / wall / 1e9
     upd = kern.get("update_gemm_f64", {})
     small = kern.get("small_c64", {})
-    per_step_ms = {k: v["ms"] / args.steps for k, v in kern.items()}
-    c4_ms = sum(v for k, v in per_step_ms.items() if k.endswith("_f64"))
-    c2_ms = per_step_ms.get("small_c64", 0.0)
+    c4_ms = sum(e[0].elapsed_time(e[1]) for e in marks) / len(marks)
+    c2_ms = sum(e[1].elapsed_time(e[2]) for e in marks) / len(marks)
 
     roofline = {
         "bound": "mfma",

@@ -79,6 +79,11 @@ typedef struct trsm_profile_record_t {
  * library (all threads, all streams).  Recording adds two event records
  * per launch and nothing else. */
 trsm_status_t trsm_profile_start(void);
+/* Record only the launches whose kind k has bit k set in kind_mask (from
+ * the next launch on; the default is every kind).  Fewer records mean fewer
+ * event records on the streams, so a timed region perturbed by profiling
+ * can be limited to the kernels it reports. */
+trsm_status_t trsm_profile_select(uint32_t kind_mask);
 /* Stop recording (records are kept until the next start). */
 trsm_status_t trsm_profile_stop(void);
 /* Number of recorded launches. */

@@ -137,6 +137,10 @@ def test_kernel_entry_points_reject_bad_arguments(T):
 
 
 def test_profiler_bookkeeping_without_launches(T):
+    T.trsm_profile_select(["update_gemm", "small"])
+    T.trsm_profile_select(None)
+    with pytest.raises(KeyError):
+        T.trsm_profile_select(["no_such_kind"])
     T.trsm_profile_start()
     assert T.trsm_profile_count() == 0
     T.trsm_profile_stop()

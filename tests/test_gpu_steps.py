@@ -137,34 +137,37 @@ LF_CASES = [
 
 @pytest.mark.parametrize("lf", ["1", "0"])
 @pytest.mark.parametrize("case", LF_CASES)
-def test_gemm_fp64_lds_free_edges(T, case, lf, monkeypatch):
-    """fp64 products on the 128 x 128 tile run the LDS-free kernel (each wave
-    streams its own operands into a register ring; TRSM_GEMM_LF=0 runs the
-    LDS-staged tile instead, so both are checked): every K modulo the 8-wide
-    chunk, K = 0, NaN stored right past K in Bm (the ragged chunk must read
-    zeros there), odd M, ragged N, the D2 split (even and odd) and several
-    beta / gamma."""
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_gemm_lds_free_edges(T, dtype, case, lf, monkeypatch):
+    """fp64 and fp32 products that fill the chip with 128 x 128 tiles run the
+    LDS-free kernels (each wave streams its own operands into a register
+    ring; TRSM_GEMM_LF=0 runs the LDS-staged tiles instead, so both are
+    checked): every K modulo the chunk (8 k for fp64, 16 for fp32), K = 0,
+    NaN stored right past K in Bm (the ragged chunk must read zeros there),
+    odd M, ragged N, the D2 split (even and odd) and several beta / gamma."""
     monkeypatch.setenv("TRSM_GEMM_LF", lf)
     M, N, K, ldpad, split, beta, gamma = case
-    # even leading dimensions of A and Bm: 16-byte aligned columns
-    pa = ldpad + (M + ldpad) % 2
-    pb = ldpad + (K + ldpad) % 2
-    gemm_case(T, "f64", M, N, K, beta, gamma, seed=K + M, ldpad=ldpad, ldpad_a=pa, ldpad_b=pb,
+    # leading dimensions of A and Bm padded to 16-byte aligned columns
+    per = 2 if dtype == "f64" else 4
+    pa = ldpad + (-(M + ldpad)) % per
+    pb = ldpad + (-(K + ldpad)) % per
+    gemm_case(T, dtype, M, N, K, beta, gamma, seed=K + M, ldpad=ldpad, ldpad_a=pa, ldpad_b=pb,
               split=split)
 
 
 @pytest.mark.parametrize("lf", ["1", "0"])
 @pytest.mark.parametrize("M,N", [(1000, 8100), (960, 8192), (1023, 8192), (1024, 8190)])
-def test_gemm_fp64_lds_free_triangular(T, M, N, lf, monkeypatch):
-    """Triangular fp64 products with at least 512 workgroups run the LDS-free
-    form (TRSM_GEMM_LF=0: the LDS tile): each wave takes the 64-row tiles i
+@pytest.mark.parametrize("dtype", ["f64", "f32"])
+def test_gemm_lds_free_triangular(T, dtype, M, N, lf, monkeypatch):
+    """Triangular fp64 and fp32 products with at least 512 workgroups run the
+    LDS-free form (TRSM_GEMM_LF=0: the LDS tile): each wave takes the 64-row tiles i
     and T-1-i of a 32-column block, each over K up to its own diagonal.
     Ragged last row tile (1000 = 15 x 64 + 40), an odd count of row tiles
     (960: the middle tile runs alone), odd M (a row pair split at the edge),
     ragged N."""
     monkeypatch.setenv("TRSM_GEMM_LF", lf)
-    pa = M % 2  # even leading dimensions: 16-byte aligned columns
-    gemm_case(T, "f64", M, N, M, 0.0, -0.75, seed=M + N, a_lower=True, ldpad_a=pa, ldpad_b=pa)
+    pa = (-M) % (2 if dtype == "f64" else 4)  # 16-byte aligned columns
+    gemm_case(T, dtype, M, N, M, 0.0, -0.75, seed=M + N, a_lower=True, ldpad_a=pa, ldpad_b=pa)
 
 
 @pytest.mark.parametrize("dtype", ["f64", "c64"])
@@ -217,3 +220,29 @@ def test_diag_inv_vs_oracle_identity_solve(T, dtype, ib):
         assert np.all(np.triu(Wt, 1) == 0), "upper triangle of the inverse must be explicit zeros"
         e = np.linalg.norm(Wt - ref) / np.linalg.norm(ref)
         assert e <= tol, (dtype, ib, t, e)
+
+
+def test_profile_records_by_kind(T):
+    """The launch profiler records every launch of a blocked solve with
+    HIP events (kind, sizes, duration), and only the selected kinds after
+    trsm_profile_select."""
+    import torch
+    L, B = make_problem("f64", 700, 90, seed=4)
+    Ad, Bd = to_dev(L), to_dev(B)
+    T.trsm_profile_select(None)
+    T.trsm_profile_start()
+    T.trsm_lln_ex(Ad, Bd, 1.0, ib=128)
+    torch.cuda.synchronize()
+    T.trsm_profile_stop()
+    kinds = [r["kind"] for r in T.profile_records()]
+    assert kinds[0] == "diag_inv" and "copy" in kinds and "update_gemm" in kinds
+    assert kinds.count("solve_gemm") == 6  # ceil(700 / 128) block rows
+    assert all(r["ms"] > 0 for r in T.profile_records())
+    T.trsm_profile_select(["update_gemm"])
+    T.trsm_profile_start()
+    T.trsm_lln_ex(Ad, Bd, 1.0, ib=128)
+    torch.cuda.synchronize()
+    T.trsm_profile_stop()
+    T.trsm_profile_select(None)
+    recs = T.profile_records()
+    assert recs and all(r["kind"] == "update_gemm" for r in recs)

@@ -40,7 +40,8 @@ EXPORTS = ("trsm_lln", "trsm_solve", "trsm_lln_strided_batched", "trsm_lln_ex", 
            "trsm_lln_select_ib",
            "trsm_status_string", "trsm_release_workspace",
            "trsm_kernel_diag_inv", "trsm_kernel_gemm",
-           "trsm_profile_start", "trsm_profile_stop", "trsm_profile_count", "trsm_profile_read")
+           "trsm_profile_start", "trsm_profile_select", "trsm_profile_stop", "trsm_profile_count",
+           "trsm_profile_read")
 
 KERNEL_KINDS = {0: "small", 1: "diag_inv", 2: "copy", 3: "solve_gemm", 4: "update_gemm", 5: "fill"}
 
@@ -87,6 +88,8 @@ def _load() -> ctypes.CDLL:
     lib.trsm_kernel_gemm.restype = ci
     lib.trsm_profile_start.argtypes = []
     lib.trsm_profile_start.restype = ci
+    lib.trsm_profile_select.argtypes = [ctypes.c_uint32]
+    lib.trsm_profile_select.restype = ci
     lib.trsm_profile_stop.argtypes = []
     lib.trsm_profile_stop.restype = ci
     lib.trsm_profile_count.argtypes = []
@@ -342,6 +345,19 @@ def trsm_kernel_gemm(A, Bm, D, *, beta=0.0, gamma=1.0, C=None, D2=None, split: i
 
 def trsm_profile_start():
     _check(lib.trsm_profile_start(), "trsm_profile_start")
+
+
+def trsm_profile_select(kinds=None):
+    """Record only launches of the given kinds (names of KERNEL_KINDS, or
+    None for every kind)."""
+    if kinds is None:
+        mask = 0xFFFFFFFF
+    else:
+        codes = {v: k for k, v in KERNEL_KINDS.items()}
+        mask = 0
+        for k in kinds:
+            mask |= 1 << codes[k]
+    _check(lib.trsm_profile_select(mask), "trsm_profile_select")
 
 
 def trsm_profile_stop():

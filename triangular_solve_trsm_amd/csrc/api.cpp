@@ -152,6 +152,7 @@ struct ProfRec {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+uint32_t g_prof_kinds = 0xffffffffu;  // bit k: record launches of kind k
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;
 
@@ -172,7 +173,7 @@ class LaunchTimer {
     LaunchTimer(int kind, int dt, int64_t m, int64_t n, int64_t k, int64_t batch, hipStream_t st)
         : st_(st) {
         std::lock_guard<std::mutex> lk(g_prof_mu);
-        if (!g_prof_on) return;
+        if (!g_prof_on || kind < 0 || kind > 31 || !((g_prof_kinds >> kind) & 1u)) return;
         rec_.r = trsm_profile_record_t{kind, dt, m, n, k, batch, 0.0f};
         rec_.start = take_event();
         rec_.stop = take_event();
@@ -722,6 +723,12 @@ trsm_status_t trsm_profile_start(void) {
     } catch (...) {
         return TRSM_STATUS_HIP_ERROR;
     }
+}
+
+trsm_status_t trsm_profile_select(uint32_t kind_mask) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_kinds = kind_mask;
+    return TRSM_STATUS_SUCCESS;
 }
 
 trsm_status_t trsm_profile_stop(void) {

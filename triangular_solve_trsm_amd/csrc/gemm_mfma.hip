@@ -791,6 +791,166 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
     }
 }
 
+// ---- fp32 products without LDS ---------------------------------------------
+// The same structure for fp32 on v_mfma_f32_16x16x4f32 (32 cycles: twice the
+// fp64 rate on half the operand bytes, so the same operand traffic per
+// cycle), in chunks of 16 k:
+//   * A: lane (c, q) loads rows 4c .. 4c + 3 of the wave's 64 at chunk
+//     k = 4q + s (s = 0..3), 16 bytes, consecutive lanes on consecutive
+//     rows; MFMA row tile a takes row 4c + a as its row c;
+//   * Bm: lane (c, q) loads k = 4q .. 4q + 3 of columns c + 16b, 16 bytes;
+//     k index q of MFMA step s is chunk k 4q + s on both sides;
+//   * the f32 result puts MFMA row 4q + v in item v, so a lane holds output
+//     rows 16q + 4v .. 16q + 4v + 3 (tiles a = 0..3): C and D move in
+//     16-byte quadruples;
+//   * the ragged last chunk zeroes the lanes whose k is past K, with 4-byte
+//     Bm loads there.
+// NBT and TRI as for gemm_lf_kernel.
+template <int RING, int NBT, bool TRI>
+__global__ __launch_bounds__(256, 1) void gemm_lf32_kernel(GemmParams<float> p) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15;
+    const int q = lane >> 4;
+    int tm, tn;
+    map_tile(blockIdx.x, p.tilesM, p.tilesN, tm, tn);
+    const float *__restrict__ pA = p.A;
+    const float *__restrict__ pB = p.Bm;
+    const int64_t lda = p.lda, ldb = p.ldb;
+    uint32_t offA[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) offA[s] = (uint32_t)((4 * c16 + (4 * q + s) * lda) * 4);
+    uint32_t offB[NBT];
+#pragma unroll
+    for (int b = 0; b < NBT; ++b) offB[b] = (uint32_t)((4 * q + (c16 + 16 * (int64_t)b) * ldb) * 4);
+    const float sc = (float)p.sc.re, gamma = (float)p.gamma.re;
+
+    auto run_tile = [&](const int64_t r0, const int64_t c0, const int64_t K) {
+        f4 acc[4][NBT];
+#pragma unroll
+        for (int b = 0; b < NBT; ++b) {
+            const int64_t j = c0 + c16 + 16 * b;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t r = r0 + 16 * q + 4 * v;
+                float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (p.has_c && j < p.N) {
+                    const float *col = p.C + j * p.ldc;
+                    if (p.c_vec && r + 3 < p.M) {
+                        const f4 c4 = *reinterpret_cast<const f4 *>(col + r);
+                        x[0] = c4[0]; x[1] = c4[1]; x[2] = c4[2]; x[3] = c4[3];
+                    } else {
+#pragma unroll
+                        for (int a = 0; a < 4; ++a)
+                            if (r + a < p.M) x[a] = col[r + a];
+                    }
+                }
+#pragma unroll
+                for (int a = 0; a < 4; ++a) acc[a][b][v] = sc * x[a];
+            }
+        }
+
+        f4 ra[RING][4], rb[RING][NBT];
+        auto load = [&](int slot, int64_t k0, bool live) {
+            const int64_t oa = r0 + k0 * lda;
+            const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, live ? (p.extA - oa) * 4 : 0);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) ra[slot][s] = __builtin_bit_cast(f4, ld16<true>(rsa, offA[s]));
+            const int64_t ob = k0 + c0 * ldb;
+            const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, live ? (p.extB - ob) * 4 : 0);
+#pragma unroll
+            for (int b = 0; b < NBT; ++b) rb[slot][b] = __builtin_bit_cast(f4, ld16<true>(rsb, offB[b]));
+        };
+        auto compute = [&](const f4 (&a4)[4], const f4 (&bq)[NBT]) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < NBT; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s][a], bq[b][s], acc[a][b], 0, 0, 0);
+        };
+        const int64_t nkf = K / 16;  // full chunks
+#pragma unroll
+        for (int u = 0; u < RING; ++u) load(u, 16 * u, u < nkf);
+        for (int64_t kc = 0; kc < nkf; kc += RING) {
+#pragma unroll
+            for (int u = 0; u < RING; ++u) {
+                if (kc + u < nkf) {  // uniform
+                    compute(ra[u], rb[u]);
+                    load(u, 16 * (kc + u + RING), kc + u + RING < nkf);
+                }
+            }
+        }
+        const int kr = (int)(K - 16 * nkf);
+        if (kr > 0) {
+            const int64_t k0 = 16 * nkf;
+            const int64_t oa = r0 + k0 * lda;
+            const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, (p.extA - oa) * 4);
+            const uint32_t dead = 0xfffffff0u;
+            f4 ta[4], tb[NBT];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                ta[s] = __builtin_bit_cast(f4, ld16<true>(rsa, 4 * q + s < kr ? offA[s] : dead));
+            const int64_t ob = k0 + c0 * ldb;
+            const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, (p.extB - ob) * 4);
+#pragma unroll
+            for (int b = 0; b < NBT; ++b)
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    tb[b][s] = __builtin_bit_cast(
+                        float, __builtin_amdgcn_raw_buffer_load_b32(rsb, 4 * q + s < kr ? offB[b] + 4 * s : dead, 0, 0));
+            compute(ta, tb);
+        }
+
+#pragma unroll
+        for (int b = 0; b < NBT; ++b) {
+            const int64_t j = c0 + c16 + 16 * b;
+            if (j >= p.N) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t r = r0 + 16 * q + 4 * v;
+                if (r >= p.M) continue;
+                float out[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) out[a] = gamma * acc[a][b][v];
+                if (r + 3 < p.M && r + 3 < p.split) {
+                    float *dst = p.D2 + j * p.ldd2 + r;
+                    if (p.d2_vec) *reinterpret_cast<f4 *>(dst) = f4{out[0], out[1], out[2], out[3]};
+                    else for (int a = 0; a < 4; ++a) dst[a] = out[a];
+                } else if (r + 3 < p.M && r >= p.split) {
+                    float *dst = p.D + j * p.ldd + r;
+                    if (p.d_vec) *reinterpret_cast<f4 *>(dst) = f4{out[0], out[1], out[2], out[3]};
+                    else for (int a = 0; a < 4; ++a) dst[a] = out[a];
+                } else {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const int64_t ii = r + a;
+                        if (ii >= p.M) break;
+                        if (ii < p.split) p.D2[ii + j * p.ldd2] = out[a];
+                        else p.D[ii + j * p.ldd] = out[a];
+                    }
+                }
+            }
+        }
+    };
+
+    if constexpr (TRI) {
+        const int T = (int)((p.M + 63) / 64);
+        const int64_t c0 = (int64_t)tn * 64 * NBT + (int64_t)wave * 16 * NBT;
+        const int t1 = T - 1 - tm;
+        for (int pass = 0; pass < (t1 != tm ? 2 : 1); ++pass) {
+            const int64_t r0 = (int64_t)(pass == 0 ? tm : t1) * 64;
+            run_tile(r0, c0, r0 + 64 < p.K ? r0 + 64 : p.K);
+        }
+    } else {
+        const int64_t r0 = (int64_t)tm * 128 + (wave & 1) * 64;
+        const int64_t c0 = (int64_t)tn * 32 * NBT + (int64_t)(wave >> 1) * 16 * NBT;
+        run_tile(r0, c0, p.K);
+    }
+}
+
 inline bool aligned16(const void *ptr, int64_t ld, size_t es) {
     return (reinterpret_cast<uintptr_t>(ptr) % 16) == 0 && ((int64_t)es * ld) % 16 == 0;
 }
@@ -946,6 +1106,26 @@ hipError_t launch_lf_tri(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// fp32 single products on gemm_lf32_kernel: the update tile 128 x 128
+// (64 x 64 per wave), the triangular product's wave tile 64 x 32.
+template <int RING, int NBT, bool TRI>
+hipError_t launch_lf32(const GemmDesc &g, hipStream_t st) {
+    GemmParams<float> p;
+    dim3 grid;
+    hipError_t e = tile_params<float, 128, 128>(g, p, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    if (TRI) {
+        p.tilesM = (int)(((g.M + 63) / 64 + 1) / 2);
+        p.tilesN = (int)((g.N + 64 * NBT - 1) / (64 * NBT));
+    } else {
+        p.tilesM = (int)((g.M + 127) / 128);
+        p.tilesN = (int)((g.N + 32 * NBT - 1) / (32 * NBT));
+    }
+    grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
+    hipLaunchKernelGGL((gemm_lf32_kernel<RING, NBT, TRI>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
 // Macro tile, from timings on MI355X of the update and solve sequences of
 // blocked solves (fp32 4096^2, fp64 1024^2 .. 8192^2, complex 8192 x 2048):
 //   * 64 x 32 for the triangular solve products (each workgroup folds two
@@ -982,6 +1162,23 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
     // complex fp64.  Measured: fp64 8192^2 9.259 -> 9.218 ms, complex
     // 8192 x 2048 9.574 -> 9.457 ms, complex 4096^2 4.904 -> 4.847 ms; with
     // fewer workgroups (fp64 4096^2: 256) the wider tile lost (1.396 -> 1.428).
+    // fp32 single products whose 128-wide tiles fill the chip run without
+    // LDS (measured on fp32 8192^2: the solve 4.56 -> 4.30 ms, updates 6 %
+    // and triangular products 7 % faster; at fp32 4096^2, which gives half
+    // as many tiles, the LDS tiles stay ahead and are kept)
+    if constexpr (std::is_same<T, float>::value) {
+        if (g.batch <= 1 && !g.b_lower && use_gemm_lf() && aligned16(g.A, g.lda, 4) &&
+            aligned16(g.Bm, g.ldb, 4)) {
+            const int64_t tN128 = (g.N + 127) / 128;
+            if (g.a_lower) {
+                if ((((g.M + 63) / 64 + 1) / 2) * tN128 >= 512) return launch_lf32<5, 2, true>(g, st);
+            } else {
+                const int64_t t128 = ((g.M + 127) / 128) * tN128;
+                if (g.M > 64 && t128 >= 512 && 4 * t128 >= 3 * 512 * ((t128 + 511) / 512))
+                    return launch_lf32<5, 4, false>(g, st);
+            }
+        }
+    }
     if (g.a_lower && !g.b_lower && g.batch <= 1) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
         const int64_t pairs = ((Mr + 63) / 64 + 1) / 2;
