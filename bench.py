@@ -105,8 +105,8 @@ def summarize_kernels(records):
 def update_tiles(records):
     """Macro tile of each fp64 update launch, by the library's rule for a
     single real fp64 product with 16-byte aligned operands (launch_sized in
-    gemm_mfma.hip): 128 x 128 when M > 64 and that gives at least 512 tiles
-    in rounds of 512 at least 3/4 full, 128 x 64
+    gemm_mfma.hip): 128 x 128 on the LDS-free kernel when M > 64 and that
+    gives at least 512 tiles in rounds of 512 at least 3/4 full, 128 x 64
     when that gives at least 2048, 64 x 32 when 64 x 64 gives fewer than
     1024, 64 x 64 otherwise."""
     counts = {}
@@ -116,7 +116,7 @@ def update_tiles(records):
         M, N = r["m"], r["n"]
         t128 = -(-M // 128) * -(-N // 128)
         if M > 64 and t128 >= 512 and 4 * t128 >= 3 * 512 * -(-t128 // 512):
-            t = "128x128"
+            t = "128x128 LDS-free (gemm_lf_kernel)"
         elif -(-M // 128) * -(-N // 64) >= 2048:
             t = "128x64"
         elif -(-M // 64) * -(-N // 64) < 1024:
@@ -472,7 +472,7 @@ def main():
 
     roofline = {
         "bound": "mfma",
-        "kernel": "update_gemm_f64 (gemm_kernel<double, tile, 16>, launches per tile: "
+        "kernel": "update_gemm_f64 (launches per tile: "
                   + ", ".join(f"{t} x{c // args.steps}" for t, c in sorted(update_tiles(recs).items()))
                   + f" per step; {phase2_order(recs)} phase 2)",
         "achieved": upd.get("tflops"),
