@@ -155,6 +155,36 @@ def test_gemm_lds_free_edges(T, dtype, case, lf, monkeypatch):
               split=split)
 
 
+LF_CPLX_CASES = [
+    # (M, N, K, ldpad, split, beta, gamma) in complex elements: the real view
+    # 2M x N gives 16 x 32 = 512 tiles of 128 x 128
+    (1000, 4000, 0, 0, 0, 1.5 - 0.5j, -1.0),        # K = 0: D = beta C
+    (1000, 4000, 1, 1, 0, 1.0, -1.0 + 0.5j),        # a single k
+    (1000, 4000, 3, 1, 0, 0.0, 0.5j),
+    (1000, 4000, 4, 0, 0, 1.0, -1.0),               # one full chunk (8 real k)
+    (1000, 4000, 5, 1, 0, 0.25j, -1.0),
+    (1000, 4000, 23, 2, 0, -0.5 + 1j, 2.0 - 1j),    # NaN in the rows of Bm past K
+    (999, 4000, 31, 1, 0, 1.0, -1.0),               # odd M
+    (1000, 4000, 64, 0, 100, 1.0, -1.0),            # rows below 100 routed to D2
+    (1000, 4000, 501, 1, 37, 0.5 + 0.25j, -1.0),    # odd split
+    (1000, 3999, 128, 0, 0, 1.0, -1.0 - 1j),        # ragged N
+]
+
+
+@pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("case", LF_CPLX_CASES)
+def test_gemm_lds_free_complex(T, case, lf, monkeypatch):
+    """Complex fp64 products that fill the chip run the LDS-free fp64 kernel
+    on their real view (each complex element of A the 2 x 2 block [[re, -im],
+    [im, re]], Bm, C and D read as interleaved real; TRSM_GEMM_LF=0: the LDS
+    tiles): every K modulo the chunk (4 complex k), K = 0, NaN right past K
+    in Bm, odd M, ragged N, the D2 split, complex beta and gamma (C and the
+    result scaled as complex numbers)."""
+    monkeypatch.setenv("TRSM_GEMM_LF", lf)
+    M, N, K, ldpad, split, beta, gamma = case
+    gemm_case(T, "c64", M, N, K, beta, gamma, seed=K + M, ldpad=ldpad, split=split)
+
+
 @pytest.mark.parametrize("lf", ["1", "0"])
 @pytest.mark.parametrize("M,N", [(1000, 8100), (960, 8192), (1023, 8192), (1024, 8190)])
 @pytest.mark.parametrize("dtype", ["f64", "f32"])

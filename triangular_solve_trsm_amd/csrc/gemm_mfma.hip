@@ -623,7 +623,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
 // only; each wave takes row tiles i and T-1-i (T = 64-row tiles) one after
 // the other, so every wave gets the same length of K (no barriers: waves
 // run independently).
-template <int RING, int NBT, bool TRI>
+// CPLX: complex fp64 through the real 2 x 2 embedding (each complex a of A
+// is [[ar, -ai], [ai, ar]]).  p describes the real view: M and K count real
+// rows and real k (twice the complex counts), Bm, C, D and D2 are their
+// interleaved storage read as real with doubled leading dimensions, split
+// counts real rows; only A keeps complex addressing (lda in complex elements,
+// extA in doubles).  One 16-byte load of complex A(i, k) gives lane (c, q)
+// the whole 2 x 2 block it feeds for complex row i: (ar, ai) on step s = 0,
+// (-ai, ar) on s = 1; a pair of output rows is one complex element, so C is
+// scaled by sc and the result by gamma as complex numbers.
+template <int RING, int NBT, bool TRI, bool CPLX = false>
 __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -637,12 +646,16 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
     const double *__restrict__ pA = p.A;
     const double *__restrict__ pB = p.Bm;
     const int64_t lda = p.lda, ldb = p.ldb;
-    const uint32_t offA0 = (uint32_t)((2 * c16 + 2 * q * lda) * 8);
+    // real: rows 2c, 2c + 1 at k = 2q (offA0) and 2q + 1 (offA1), 32 rows
+    // further at +256 bytes; complex: element (c, q) and 16 complex rows
+    // further (+256 bytes)
+    const uint32_t offA0 = CPLX ? (uint32_t)((c16 + q * lda) * 16) : (uint32_t)((2 * c16 + 2 * q * lda) * 8);
     const uint32_t offA1 = offA0 + (uint32_t)(lda * 8);
     uint32_t offB[NBT];
 #pragma unroll
     for (int b = 0; b < NBT; ++b) offB[b] = (uint32_t)((2 * q + (c16 + 16 * (int64_t)b) * ldb) * 8);
     const double sc = p.sc.re, gamma = p.gamma.re;
+    const double sci = p.sc.im, gammai = p.gamma.im;  // complex only
 
     // the wave's output block: rows [r0, r0 + 64), columns [c0, c0 + 16 NBT),
     // products over k in [0, K)
@@ -671,8 +684,16 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
                         }
                     }
                 }
+                if constexpr (CPLX) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) acc[a][b][v] = sc * x[a];
+                    for (int h = 0; h < 2; ++h) {  // complex sc * C
+                        acc[2 * h][b][v] = sc * x[2 * h] - sci * x[2 * h + 1];
+                        acc[2 * h + 1][b][v] = sc * x[2 * h + 1] + sci * x[2 * h];
+                    }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) acc[a][b][v] = sc * x[a];
+                }
             }
         }
 
@@ -681,12 +702,15 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
         // chunk [k0, k0 + 8) into ring slot `slot`; live == false issues the
         // loads on an empty range (no memory access, zeros)
         auto load = [&](int slot, int64_t k0, bool live) {
+            // complex: element (r0/2, k0/2) sits at double offset r0 + k0 lda
             const int64_t oa = r0 + k0 * lda;
             const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, live ? (p.extA - oa) * 8 : 0);
             ra[slot][0] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0));
             ra[slot][1] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0 + 256));
-            ra[slot][2] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1));
-            ra[slot][3] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1 + 256));
+            if constexpr (!CPLX) {
+                ra[slot][2] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1));
+                ra[slot][3] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1 + 256));
+            }
             const int64_t ob = k0 + c0 * ldb;
             const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, live ? (p.extB - ob) * 8 : 0);
 #pragma unroll
@@ -695,7 +719,16 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
         auto compute = [&](const d2v (&a4)[4], const d2v (&bq)[NBT]) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                const double av[4] = {a4[2 * s][0], a4[2 * s][1], a4[2 * s + 1][0], a4[2 * s + 1][1]};
+                double av[4];
+                if constexpr (CPLX) {
+                    if (s == 0) {
+                        av[0] = a4[0][0]; av[1] = a4[0][1]; av[2] = a4[1][0]; av[3] = a4[1][1];
+                    } else {
+                        av[0] = -a4[0][1]; av[1] = a4[0][0]; av[2] = -a4[1][1]; av[3] = a4[1][0];
+                    }
+                } else {
+                    av[0] = a4[2 * s][0]; av[1] = a4[2 * s][1]; av[2] = a4[2 * s + 1][0]; av[3] = a4[2 * s + 1][1];
+                }
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -728,15 +761,21 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
             d2v ta[4], tb[NBT];
             ta[0] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok0 ? offA0 : dead));
             ta[1] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok0 ? offA0 + 256 : dead));
-            ta[2] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 : dead));
-            ta[3] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 + 256 : dead));
             const int64_t ob = k0 + c0 * ldb;
             const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, (p.extB - ob) * 8);
+            if constexpr (CPLX) {
+                // the real K is even: a complex k is whole or absent
 #pragma unroll
-            for (int b = 0; b < NBT; ++b) {
-                const u2v lo = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok0 ? offB[b] : dead, 0, 0);
-                const u2v hi = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok1 ? offB[b] + 8 : dead, 0, 0);
-                tb[b] = d2v{__builtin_bit_cast(double, lo), __builtin_bit_cast(double, hi)};
+                for (int b = 0; b < NBT; ++b) tb[b] = __builtin_bit_cast(d2v, ld16<true>(rsb, ok0 ? offB[b] : dead));
+            } else {
+                ta[2] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 : dead));
+                ta[3] = __builtin_bit_cast(d2v, ld16<true>(rsa, ok1 ? offA1 + 256 : dead));
+#pragma unroll
+                for (int b = 0; b < NBT; ++b) {
+                    const u2v lo = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok0 ? offB[b] : dead, 0, 0);
+                    const u2v hi = __builtin_amdgcn_raw_buffer_load_b64(rsb, ok1 ? offB[b] + 8 : dead, 0, 0);
+                    tb[b] = d2v{__builtin_bit_cast(double, lo), __builtin_bit_cast(double, hi)};
+                }
             }
             compute(ta, tb);
         }
@@ -752,8 +791,14 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
                 for (int h = 0; h < 2; ++h) {
                     const int64_t r = r0 + 2 * (q + 4 * v) + 32 * h;
                     if (r >= p.M) continue;
-                    const double x0 = gamma * acc[2 * h][b][v];
-                    const double x1 = gamma * acc[2 * h + 1][b][v];
+                    double x0, x1;
+                    if constexpr (CPLX) {  // complex gamma * acc
+                        x0 = gamma * acc[2 * h][b][v] - gammai * acc[2 * h + 1][b][v];
+                        x1 = gamma * acc[2 * h + 1][b][v] + gammai * acc[2 * h][b][v];
+                    } else {
+                        x0 = gamma * acc[2 * h][b][v];
+                        x1 = gamma * acc[2 * h + 1][b][v];
+                    }
                     if (r + 1 < p.M && r + 1 < p.split) {
                         double *dst = p.D2 + j * p.ldd2 + r;
                         if (p.d2_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
@@ -1087,6 +1132,45 @@ hipError_t launch_lf(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Complex fp64 single products on gemm_lf_kernel through the real view.
+hipError_t launch_lf_cplx(const GemmDesc &g, hipStream_t st) {
+    GemmParams<cplx> pc;
+    dim3 grid;
+    hipError_t e = tile_params<cplx, 128, 128>(g, pc, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    GemmParams<double> p{};
+    p.M = 2 * pc.M;
+    p.N = pc.N;
+    p.K = 2 * pc.K;
+    p.A = reinterpret_cast<const double *>(pc.A);
+    p.lda = pc.lda;  // complex elements (A keeps complex addressing)
+    p.extA = 2 * pc.extA;
+    p.Bm = reinterpret_cast<const double *>(pc.Bm);
+    p.ldb = 2 * pc.ldb;
+    p.extB = 2 * pc.extB;
+    p.C = reinterpret_cast<const double *>(pc.C);
+    p.ldc = 2 * pc.ldc;
+    p.D = reinterpret_cast<double *>(pc.D);
+    p.ldd = 2 * pc.ldd;
+    p.D2 = reinterpret_cast<double *>(pc.D2);
+    p.ldd2 = 2 * pc.ldd2;
+    p.split = 2 * pc.split;
+    p.sc = pc.sc;
+    p.gamma = pc.gamma;
+    p.has_c = pc.has_c;
+    p.a_vec = pc.a_vec;
+    p.b_vec = pc.b_vec;
+    p.c_vec = pc.c_vec;
+    p.d_vec = pc.d_vec;
+    p.d2_vec = pc.d2_vec;
+    p.tilesM = (int)((p.M + 127) / 128);
+    p.tilesN = (int)((p.N + 127) / 128);
+    p.binner = 1;
+    grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
+    hipLaunchKernelGGL((gemm_lf_kernel<3, 4, false, true>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
 // Triangular fp64 product (the diagonal-block solve): workgroups of four
 // 64 x 32 waves over 128 columns, each wave on the row-tile pair (i, T-1-i),
 // with a ring of five chunks.  Measured on the 1024 x 8192 solve of fp64
@@ -1196,6 +1280,17 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
     if (g.a_lower || g.b_lower) return launch_tile<T, 64, 32, KT>(g, st);
     if (g.batch <= 1) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
+        if constexpr (std::is_same<T, cplx>::value) {
+            // real view 2M x N on 128 x 128 tiles without LDS, under the
+            // fp64 rule (at least 512 tiles, rounds at least 3/4 full);
+            // TRSM_LF_CPLX=0 keeps the LDS tiles (tuning)
+            const int64_t t128 = ((Mr + 127) / 128) * ((g.N + 127) / 128);
+            const char *ec = std::getenv("TRSM_LF_CPLX");
+            if (use_gemm_lf() && !(ec && ec[0] == '0') && t128 >= 512 &&
+                4 * t128 >= 3 * 512 * ((t128 + 511) / 512) && aligned16(g.A, g.lda, 16) &&
+                aligned16(g.Bm, g.ldb, 16))
+                return launch_lf_cplx(g, st);
+        }
         if constexpr (GemmTraits<T>::kCplx) {
             if (((Mr + 63) / 64) * ((g.N + 127) / 128) >= 2048) return launch_tile<T, 64, 128, KT>(g, st);
         } else if constexpr (sizeof(T) == 8) {
