@@ -43,6 +43,9 @@
 // right of it inside the ib block): the doubling step's products and the
 // triangular GEMM of the solve phase skip only whole zero K tiles and rely
 // on the zeros inside the tiles they do read.
+#include <cstdlib>
+#include <cstring>
+
 #include "buffer_ops.h"
 #include "scalar_ops.h"
 
@@ -264,6 +267,295 @@ hipError_t launch_base(int dtype, int64_t m, const void *A, int64_t lda, void *W
     }
 }
 
+// ---- fused base: whole NB x NB diagonal blocks in LDS ----------------------
+// One workgroup (four waves) inverts one NB x NB diagonal block (NB = 128,
+// or 64 for complex fp64, whose 128-block would not fit in LDS):
+//   1. the block's lower triangle is loaded into LDS (zeros above the
+//      diagonal, identity past the end of L);
+//   2. its 16 x 16 diagonal blocks are inverted by substitution, one lane
+//      per column (16 steps, each a short dot product with the solved rows);
+//   3. recursive doubling 16 -> 32 -> .. -> NB inside LDS, X21 = -W22 L21 W11
+//      for every pair of neighbouring blocks, both products on the matrix
+//      cores (16 x 16 output tiles over the four waves, the zero half of the
+//      triangular factor skipped); the product W22 L21 is kept in the pair's
+//      upper-right quadrant, which is zero in the result and is cleared
+//      again after use;
+//   4. the block is written to W.
+// So the 64 x 64 substitution and the first doubling level (two batched
+// launches) become one launch whose serial chain is 16 steps long.
+// Workgroups past the blocks write the zeros right of each block inside its
+// ib x ib parent, 64 columns each, alongside.
+template <typename T> struct InvMma;
+template <> struct InvMma<float> {
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    struct Acc { v4 a; };
+    __device__ __forceinline__ static void zero(Acc &c) { c.a = v4{0.f, 0.f, 0.f, 0.f}; }
+    __device__ __forceinline__ static void mma(float x, float y, Acc &c) {
+        c.a = __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, c.a, 0, 0, 0);
+    }
+    __device__ __forceinline__ static float get(const Acc &c, int v) { return c.a[v]; }
+    // output row of item v in lane group q (f32 result layout)
+    __device__ __forceinline__ static int row(int q, int v) { return 4 * q + v; }
+};
+template <> struct InvMma<double> {
+    typedef double v4 __attribute__((ext_vector_type(4)));
+    struct Acc { v4 a; };
+    __device__ __forceinline__ static void zero(Acc &c) { c.a = v4{0.0, 0.0, 0.0, 0.0}; }
+    __device__ __forceinline__ static void mma(double x, double y, Acc &c) {
+        c.a = __builtin_amdgcn_mfma_f64_16x16x4f64(x, y, c.a, 0, 0, 0);
+    }
+    __device__ __forceinline__ static double get(const Acc &c, int v) { return c.a[v]; }
+    __device__ __forceinline__ static int row(int q, int v) { return q + 4 * v; }  // f64 layout
+};
+// complex: four real products (re += xr yr - xi yi, im += xr yi + xi yr)
+template <typename C, typename R> struct InvMmaCplx {
+    using Re = InvMma<R>;
+    struct Acc { typename Re::Acc re, im; };
+    __device__ __forceinline__ static void zero(Acc &c) { Re::zero(c.re); Re::zero(c.im); }
+    __device__ __forceinline__ static void mma(C x, C y, Acc &c) {
+        Re::mma(x.re, y.re, c.re);
+        Re::mma(-x.im, y.im, c.re);
+        Re::mma(x.re, y.im, c.im);
+        Re::mma(x.im, y.re, c.im);
+    }
+    __device__ __forceinline__ static C get(const Acc &c, int v) { return C{Re::get(c.re, v), Re::get(c.im, v)}; }
+    __device__ __forceinline__ static int row(int q, int v) { return Re::row(q, v); }
+};
+template <> struct InvMma<cplx> : InvMmaCplx<cplx, double> {};
+template <> struct InvMma<cplx32> : InvMmaCplx<cplx32, float> {};
+
+// 1/d without a branch (the same values as Elem<T>::recip: a real complex
+// divisor gives the exactly rounded real reciprocal); a branch per row of the
+// unrolled substitution below split it into divergent blocks whose reads of
+// L the compiler then held in registers all at once
+__device__ __forceinline__ float recip_nb(float d) { return 1.0f / d; }
+__device__ __forceinline__ double recip_nb(double d) { return 1.0 / d; }
+__device__ __forceinline__ cplx recip_nb(cplx d) {
+    const double den = d.re * d.re + d.im * d.im;
+    const bool real = d.im == 0.0;
+    return cplx{real ? 1.0 / d.re : d.re / den, real ? 0.0 : -d.im / den};
+}
+__device__ __forceinline__ cplx32 recip_nb(cplx32 d) {
+    const float den = d.re * d.re + d.im * d.im;
+    const bool real = d.im == 0.0f;
+    return cplx32{real ? 1.0f / d.re : d.re / den, real ? 0.0f : -d.im / den};
+}
+
+__device__ __forceinline__ float neg(float x) { return -x; }
+__device__ __forceinline__ double neg(double x) { return -x; }
+__device__ __forceinline__ cplx neg(cplx x) { return cplx{-x.re, -x.im}; }
+__device__ __forceinline__ cplx32 neg(cplx32 x) { return cplx32{-x.re, -x.im}; }
+
+template <typename T, int NB>
+__global__ __launch_bounds__(256) void inv_block_kernel(int64_t m, const T *__restrict__ A, int64_t lda,
+                                                        T *__restrict__ W, int ldw, int nblk, int nzc) {
+    using E = Elem<T>;
+    using M = InvMma<T>;
+    constexpr int LD = NB + 1;  // LDS column stride
+    constexpr bool kCplx = sizeof(T) > sizeof(typename E::Real);
+    __shared__ T S[NB * LD];
+    // complex: the 16 x 16 inverses are built in LDS (register arrays of
+    // complex values made the compiler spill)
+    __shared__ T Wsub[kCplx ? NB * 16 : 1];
+    const int tid = threadIdx.x;
+    const int bid = blockIdx.x;
+    const int64_t W2 = (int64_t)ldw * ldw;
+
+    if (bid >= nblk) {
+        // zeros in rows [lo, lo + NB) of the parent, columns right of the block
+        const int z = bid - nblk;
+        const int t = z / nzc, cc = z - (z / nzc) * nzc;
+        const int64_t base = (int64_t)t * NB;
+        const int64_t tp = base / ldw;
+        const int lo = (int)(base - tp * ldw);
+        const int bsp = (int)((m - tp * ldw) < ldw ? (m - tp * ldw) : ldw);
+        const int rows = (bsp - lo) < NB ? (bsp - lo) : NB;
+        const int c0 = lo + NB + 64 * cc;
+        const int c1 = (c0 + 64) < bsp ? (c0 + 64) : bsp;
+        if (rows <= 0 || c0 >= c1) return;
+        T *Wp = W + tp * W2;
+        for (int e = tid; e < NB * 64; e += 256) {
+            const int i = e % NB, j = e / NB;
+            if (i < rows && c0 + j < c1) Wp[(lo + i) + (int64_t)(c0 + j) * ldw] = E::zero();
+        }
+        return;
+    }
+
+    const int64_t base = (int64_t)bid * NB;
+    const int bs = (int)((m - base) < NB ? (m - base) : NB);
+    const int64_t tp = base / ldw;
+    const int lo = (int)(base - tp * ldw);
+    T *__restrict__ Wt = W + tp * W2 + (int64_t)lo * (ldw + 1);
+    const T *__restrict__ Ad = A + base + base * lda;
+
+    // 1. lower triangle into LDS; every address read lies inside L (indices
+    // clamped to the block), so the loads need no condition and all of them
+    // are issued before the first LDS write (one memory latency, not one per
+    // group of loads)
+    {
+        constexpr int PER = NB * NB / 256;
+        T x[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + 256 * u;
+            const int i = e % NB, j = e / NB;
+            const int ic = i < bs ? i : bs - 1, jc = j < bs ? j : bs - 1;
+            x[u] = Ad[ic + (int64_t)jc * lda];
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + 256 * u;
+            const int i = e % NB, j = e / NB;
+            const bool in = i < bs && j < bs;
+            S[i + j * LD] = E::sel(i >= j && in, x[u], E::sel(i == j, E::one(), E::zero()));
+        }
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15;
+    const int q = lane >> 4;
+
+    // 2. 16 x 16 diagonal blocks: block d = 4 * wave + q, column j = c16.
+    // Row i of column j: (e_j - sum_{k < i} l_ik w_kj) / l_ii; rows above j
+    // are zero (set, not computed: a zero l_kk must not turn them into NaN).
+    if constexpr (kCplx) {
+        const int d = 4 * wave + q;
+        if (d < NB / 16) {
+            T *Ld = S + d * 16 * (LD + 1);
+            T *Wl = Wsub + d * 256 + c16 * 16;  // column c16 of this block's inverse
+            for (int i = 0; i < 16; ++i) {
+                T acc = E::sel(i == c16, E::one(), E::zero());
+#pragma unroll 4
+                for (int k = c16; k < i; ++k) acc = E::msub(acc, Ld[i + k * LD], Wl[k]);
+                Wl[i] = E::sel(i >= c16, E::mul(acc, recip_nb(Ld[i + i * LD])), E::zero());
+            }
+            // every lane of the block's group has finished reading L (one
+            // wave, in order) before its column is written over L's
+            for (int i = 0; i < 16; ++i) Ld[i + c16 * LD] = Wl[i];
+        }
+    } else {
+        const int d = 4 * wave + q;
+        if (d < NB / 16) {
+            T *Ld = S + d * 16 * (LD + 1);
+            T w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                T acc = E::sel(i == c16, E::one(), E::zero());
+#pragma unroll
+                for (int k = 0; k < i; ++k) acc = E::msub(acc, Ld[i + k * LD], w[k]);
+                w[i] = E::sel(i >= c16, E::mul(acc, recip_nb(Ld[i + i * LD])), E::zero());
+                // one row at a time: hoisting every row's reads of L would
+                // hold 136 elements in registers (spills for complex types)
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Ld[i + c16 * LD] = w[i];
+        }
+    }
+    __syncthreads();
+
+    // 3. doubling: pairs of b x b blocks at o = 2 b p
+#pragma unroll
+    for (int b = 16; b < NB; b *= 2) {
+        const int nt = b / 16;           // tiles per side
+        const int ntile = (NB / (2 * b)) * nt * nt;
+        // T = W22 L21 into the upper-right quadrant (W22 lower: k < 16 (ti + 1));
+        // tile t of a pair is (t / nt, t % nt), so the waves (t = wave + 4i)
+        // share out the row tiles, whose K differs, evenly
+        for (int t = wave; t < ntile; t += 4) {
+            const int pr = t / (nt * nt), tt = t - pr * nt * nt;
+            const int ti = tt / nt, tj = tt - ti * nt;
+            const int o = 2 * b * pr;
+            const T *Aw = S + (o + b) + (o + b) * LD + ti * 16;
+            const T *Bl = S + (o + b) + o * LD + tj * 16 * LD;
+            typename M::Acc acc;
+            M::zero(acc);
+            for (int k0 = 0; k0 < 16 * (ti + 1); k0 += 16)  // 16 k per step: four products
+#pragma unroll
+                for (int kk = k0; kk < k0 + 16; kk += 4)
+                    M::mma(Aw[c16 + (kk + q) * LD], Bl[(kk + q) + c16 * LD], acc);
+            T *Dq = S + o + (o + b) * LD + ti * 16 + tj * 16 * LD;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Dq[M::row(q, v) + c16 * LD] = M::get(acc, v);
+        }
+        __syncthreads();
+        // X21 = -T W11 over L21 (W11 lower: k >= 16 tj); here the column
+        // tiles differ in K, so tile t of a pair is (t % nt, t / nt)
+        for (int t = wave; t < ntile; t += 4) {
+            const int pr = t / (nt * nt), tt = t - pr * nt * nt;
+            const int tj = tt / nt, ti = tt - tj * nt;
+            const int o = 2 * b * pr;
+            const T *Aq = S + o + (o + b) * LD + ti * 16;
+            const T *Bw = S + o + o * LD + tj * 16 * LD;
+            typename M::Acc acc;
+            M::zero(acc);
+            for (int k0 = 16 * tj; k0 < b; k0 += 16)
+#pragma unroll
+                for (int kk = k0; kk < k0 + 16; kk += 4)
+                    M::mma(Aq[c16 + (kk + q) * LD], Bw[(kk + q) + c16 * LD], acc);
+            T *Dx = S + (o + b) + o * LD + ti * 16 + tj * 16 * LD;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Dx[M::row(q, v) + c16 * LD] = neg(M::get(acc, v));
+        }
+        __syncthreads();
+        // the quadrants used for T are zero in the inverse
+        for (int e = tid; e < (NB / (2 * b)) * b * b; e += 256) {
+            const int pr = e / (b * b), r = e - pr * b * b;
+            const int i = r % b, j = r / b;
+            S[(2 * b * pr + i) + (2 * b * pr + b + j) * LD] = E::zero();
+        }
+        __syncthreads();
+    }
+
+    // 4. the block (zeros above its diagonal included) into W
+#pragma unroll 8
+    for (int e = tid; e < NB * NB; e += 256) {
+        const int i = e % NB, j = e / NB;
+        if (i < bs && j < bs) Wt[i + (int64_t)j * ldw] = S[i + j * LD];
+    }
+}
+
+template <typename T, int NB>
+hipError_t launch_block(int64_t m, const void *A, int64_t lda, void *W, int ldw, hipStream_t st) {
+    const int64_t nblk = (m + NB - 1) / NB;
+    if (nblk <= 0) return hipSuccess;
+    if (ldw % NB != 0) return hipErrorInvalidValue;
+    const int nzc = (ldw - NB) / 64;  // zero tasks per block (columns right of it, 64 each)
+    const int64_t grid = nblk * (1 + nzc);
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((inv_block_kernel<T, NB>), dim3((unsigned)grid), dim3(256), 0, st, m,
+                       static_cast<const T *>(A), lda, static_cast<T *>(W), ldw, (int)nblk, nzc > 0 ? nzc : 1);
+    return hipGetLastError();
+}
+
+// Block size of the fused base: 128, 64 for complex fp64 (LDS), never
+// more than ib.
+int fused_base(int dtype, int ib) {
+    const int nb = dtype == C64F ? 64 : 128;
+    return ib < nb ? ib : nb;
+}
+
+bool use_fused_base() {
+    const char *e = std::getenv("TRSM_INV_BASE");
+    return !(e && std::strcmp(e, "subst") == 0);
+}
+
+hipError_t launch_fused(int dtype, int nbase, int64_t m, const void *A, int64_t lda, void *W, int ldw,
+                        hipStream_t st) {
+    switch (dtype) {
+        case R32F: return nbase == 128 ? launch_block<float, 128>(m, A, lda, W, ldw, st)
+                                       : launch_block<float, 64>(m, A, lda, W, ldw, st);
+        case R64F: return nbase == 128 ? launch_block<double, 128>(m, A, lda, W, ldw, st)
+                                       : launch_block<double, 64>(m, A, lda, W, ldw, st);
+        case C32F: return nbase == 128 ? launch_block<cplx32, 128>(m, A, lda, W, ldw, st)
+                                       : launch_block<cplx32, 64>(m, A, lda, W, ldw, st);
+        case C64F: return launch_block<cplx, 64>(m, A, lda, W, ldw, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 int64_t diag_inv_tmp_elems(int ib, int64_t m) {
@@ -276,8 +568,17 @@ hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t 
                            void *tmp, hipStream_t stream) {
     if (ib != 64 && ib != 128 && ib != 256 && ib != 512 && ib != 1024) return hipErrorInvalidValue;
     if (m <= 0) return hipSuccess;
-    hipError_t e = launch_base(dtype, m, A, lda, W, ib, stream);
-    if (e != hipSuccess || ib <= kBase) return e;
+    // the base blocks: the fused NB x NB kernel (TRSM_INV_BASE=subst: the
+    // 64 x 64 substitution, for comparison), then doubling from there
+    int nbase = kBase;
+    hipError_t e;
+    if (use_fused_base()) {
+        nbase = fused_base(dtype, ib);
+        e = launch_fused(dtype, nbase, m, A, lda, W, ib, stream);
+    } else {
+        e = launch_base(dtype, m, A, lda, W, ib, stream);
+    }
+    if (e != hipSuccess || ib <= nbase) return e;
     if (tmp == nullptr) return hipErrorInvalidValue;
     const int64_t es = (int64_t)dtype_size(dtype);
     const int64_t nb = (m + ib - 1) / ib;
@@ -286,7 +587,7 @@ hipError_t diag_inv_launch(int dtype, int ib, int64_t m, const void *A, int64_t 
     char *Wb = static_cast<char *>(W);
     char *Tb = static_cast<char *>(tmp);
     const Scalar zero{0.0, 0.0}, one{1.0, 0.0}, minus_one{-1.0, 0.0};
-    for (int64_t b = kBase; b < ib; b *= 2) {
+    for (int64_t b = nbase; b < ib; b *= 2) {
         // pairs of b x b blocks: pair (zo, zi) starts at row/column
         // o = zo*ib + zi*2b; W11 at (o, o), W22 and L22 at (o+b, o+b),
         // L21 and X21 at (o+b, o); the product W22 L21 goes to tmp

@@ -1251,12 +1251,18 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
     // and triangular products 7 % faster; at fp32 4096^2, which gives half
     // as many tiles, the LDS tiles stay ahead and are kept)
     if constexpr (std::is_same<T, float>::value) {
-        if (g.batch <= 1 && !g.b_lower && use_gemm_lf() && aligned16(g.A, g.lda, 4) &&
-            aligned16(g.Bm, g.ldb, 4)) {
+        if (g.batch <= 1 && !g.b_lower) {
+            const bool lf = use_gemm_lf() && aligned16(g.A, g.lda, 4) && aligned16(g.Bm, g.ldb, 4);
             const int64_t tN128 = (g.N + 127) / 128;
             if (g.a_lower) {
-                if ((((g.M + 63) / 64 + 1) / 2) * tN128 >= 512) return launch_lf32<5, 2, true>(g, st);
-            } else {
+                const int64_t pairs = ((g.M + 63) / 64 + 1) / 2;
+                if (lf && pairs * tN128 >= 512) return launch_lf32<5, 2, true>(g, st);
+                // fewer workgroups: the LDS tile, 64 x 64 while that still
+                // gives 512 folded workgroups (fp32 4096^2: the 1024 x 4096
+                // solve 48.5 -> 46 us against 64 x 32, the whole solve 0.706
+                // -> 0.694 ms)
+                if (pairs * ((g.N + 63) / 64) >= 512) return launch_tile<T, 64, 64, KT>(g, st);
+            } else if (lf) {
                 const int64_t t128 = ((g.M + 127) / 128) * tN128;
                 if (g.M > 64 && t128 >= 512 && 4 * t128 >= 3 * 512 * ((t128 + 511) / 512))
                     return launch_lf32<5, 4, false>(g, st);
