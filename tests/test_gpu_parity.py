@@ -255,6 +255,28 @@ def test_split_k_bidiagonal_exact(T, dtype, schedule, monkeypatch):
     assert np.array_equal(X, np.cumsum(B, axis=0)), f"{dtype} {schedule}"
 
 
+@pytest.mark.parametrize("ks", ["1", "0"])
+@pytest.mark.parametrize("dtype", ["f64", "c64"])
+@pytest.mark.parametrize("schedule", ["left", "right"])
+@pytest.mark.parametrize("m,n,ib", [(2100, 48, 512), (3000, 64, 1024), (1300, 5, 256), (2048, 33, 1024)])
+def test_split_k_inside_workgroup(T, dtype, schedule, m, n, ib, ks, monkeypatch):
+    """Products that split K (narrow B, a long K) run in fp64 and complex
+    fp64 as one launch whose waves split K inside a workgroup and add
+    their sums through LDS in a fixed order (TRSM_GEMM_KS=0: batched
+    partial products and a reduction kernel).  Both against the oracle,
+    ragged last block rows and column tiles, both phase-2 orders, split-K
+    forced on every product that can take it; the two forms agree to
+    rounding."""
+    monkeypatch.setenv("TRSM_SCHEDULE", schedule)
+    monkeypatch.setenv("TRSM_SPLITK", "65536")
+    monkeypatch.setenv("TRSM_GEMM_KS", ks)
+    print(f"case {dtype} {schedule} m={m} n={n} ib={ib} ks={ks}", flush=True)
+    L, B = make_problem(dtype, m, n, seed=m + 3 * n)
+    a = 0.75 + 0.25j if dtype in CPLX else 0.75
+    X = solve_gpu(T, L, B, a, ib=ib)
+    check(dtype, X, oracle.solve(L, B, a), f"{dtype} {schedule} m={m} n={n} ib={ib} ks={ks}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 def test_m_4097_narrow(T, dtype):
     m, n = 4097, 19

@@ -836,6 +836,171 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
     }
 }
 
+// ---- fp64 products split along K inside one workgroup --------------------
+// A narrow B gives the blocked path's products few output tiles and a long
+// K (fp64 8192 x 64 at IB 1024: a 7168 x 64 update with K = 1024, 1024 x 64
+// triangular solves with K up to 1024).  The split-K form (a batch of
+// partial products, then a reduction kernel) pays a second launch and
+// writes and reads its partial sums through memory.  gemm_ks_kernel keeps
+// the split inside one workgroup: its KW waves compute the same 64 x 16
+// output tile, wave w over the w-th of KW equal runs of 8-k chunks (the
+// fragment layout of gemm_lf_kernel with one column tile), then waves 1 ..
+// KW-1 leave their sums in LDS and wave 0 adds them in wave order (the same
+// order on every call) to its own, which started from sc * C, and writes D.
+// TRI: A lower triangular (the diagonal-block solve): the tile at r0 needs K
+// up to r0 + 64 only.  CPLX: complex fp64 through the real view, with p set
+// up as for gemm_lf_kernel.  K (real) is a multiple of 8.
+template <int RING, int KW, bool TRI, bool CPLX>
+__global__ __launch_bounds__(64 * KW) void gemm_ks_kernel(GemmParams<double> p) {
+    __shared__ double red[(KW - 1) * 16 * 64];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15;
+    const int q = lane >> 4;
+    int tm, tn;
+    map_tile(blockIdx.x, p.tilesM, p.tilesN, tm, tn);
+    const double *__restrict__ pA = p.A;
+    const double *__restrict__ pB = p.Bm;
+    const int64_t lda = p.lda, ldb = p.ldb;
+    // as gemm_lf_kernel: real rows 2c, 2c + 1 at k = 2q (offA0) and 2q + 1
+    // (offA1), 32 rows further at +256 bytes; complex element (c, q)
+    const uint32_t offA0 = CPLX ? (uint32_t)((c16 + q * lda) * 16) : (uint32_t)((2 * c16 + 2 * q * lda) * 8);
+    const uint32_t offA1 = offA0 + (uint32_t)(lda * 8);
+    const uint32_t offB = (uint32_t)((2 * q + c16 * ldb) * 8);
+    const double sc = p.sc.re, sci = p.sc.im, gamma = p.gamma.re, gammai = p.gamma.im;
+    const int64_t r0 = (int64_t)tm * 64;
+    const int64_t c0 = (int64_t)tn * 16;
+    // K is a multiple of 8 (the launcher's condition): whole chunks only
+    const int64_t K = TRI ? (r0 + 64 < p.K ? r0 + 64 : p.K) : p.K;
+    const int64_t nch = K / 8;
+    const int64_t kc0 = nch * wave / KW, kfe = nch * (wave + 1) / KW;  // this wave's chunks
+
+    d4 acc[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) acc[a] = d4{0.0, 0.0, 0.0, 0.0};
+    const int64_t j = c0 + c16;
+    if (wave == 0 && p.has_c && j < p.N) {  // wave 0 starts from sc * C
+        const double *col = p.C + j * p.ldc;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t r = r0 + 2 * (q + 4 * v) + 32 * h;
+                double x0 = 0.0, x1 = 0.0;
+                if (p.c_vec && r + 1 < p.M) {
+                    const d2v c2 = *reinterpret_cast<const d2v *>(col + r);
+                    x0 = c2[0];
+                    x1 = c2[1];
+                } else {
+                    if (r < p.M) x0 = col[r];
+                    if (r + 1 < p.M) x1 = col[r + 1];
+                }
+                if constexpr (CPLX) {
+                    acc[2 * h][v] = sc * x0 - sci * x1;
+                    acc[2 * h + 1][v] = sc * x1 + sci * x0;
+                } else {
+                    acc[2 * h][v] = sc * x0;
+                    acc[2 * h + 1][v] = sc * x1;
+                }
+            }
+        }
+    }
+
+    d2v ra[RING][4], rb[RING];
+    auto load = [&](int slot, int64_t kc, bool live) {
+        const int64_t k0 = 8 * kc;
+        const int64_t oa = r0 + k0 * lda;
+        const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, live ? (p.extA - oa) * 8 : 0);
+        ra[slot][0] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0));
+        ra[slot][1] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA0 + 256));
+        if constexpr (!CPLX) {
+            ra[slot][2] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1));
+            ra[slot][3] = __builtin_bit_cast(d2v, ld16<true>(rsa, offA1 + 256));
+        }
+        const int64_t ob = k0 + c0 * ldb;
+        const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, live ? (p.extB - ob) * 8 : 0);
+        rb[slot] = __builtin_bit_cast(d2v, ld16<true>(rsb, offB));
+    };
+    auto compute = [&](const d2v (&a4)[4], const d2v &bq) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            double av[4];
+            if constexpr (CPLX) {
+                if (s == 0) {
+                    av[0] = a4[0][0]; av[1] = a4[0][1]; av[2] = a4[1][0]; av[3] = a4[1][1];
+                } else {
+                    av[0] = -a4[0][1]; av[1] = a4[0][0]; av[2] = -a4[1][1]; av[3] = a4[1][0];
+                }
+            } else {
+                av[0] = a4[2 * s][0]; av[1] = a4[2 * s][1]; av[2] = a4[2 * s + 1][0]; av[3] = a4[2 * s + 1][1];
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a) acc[a] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bq[s], acc[a], 0, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < RING; ++u) load(u, kc0 + u, kc0 + u < kfe);
+    for (int64_t kc = kc0; kc < kfe; kc += RING) {
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+            if (kc + u < kfe) {  // uniform
+                compute(ra[u], rb[u]);
+                load(u, kc + u + RING, kc + u + RING < kfe);
+            }
+        }
+    }
+    // ---- the waves' sums into wave 0, in wave order ------------------------
+    if (wave > 0) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) red[((wave - 1) * 16 + 4 * a + v) * 64 + lane] = acc[a][v];
+    }
+    __syncthreads();
+    if (wave != 0 || j >= p.N) return;
+#pragma unroll 1
+    for (int w = 1; w < KW; ++w)  // one wave's sums at a time (registers)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[a][v] += red[((w - 1) * 16 + 4 * a + v) * 64 + lane];
+
+    // ---- D = gamma * acc, rows below `split` to D2 (as gemm_lf_kernel) ------
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t r = r0 + 2 * (q + 4 * v) + 32 * h;
+            if (r >= p.M) continue;
+            double x0, x1;
+            if constexpr (CPLX) {
+                x0 = gamma * acc[2 * h][v] - gammai * acc[2 * h + 1][v];
+                x1 = gamma * acc[2 * h + 1][v] + gammai * acc[2 * h][v];
+            } else {
+                x0 = gamma * acc[2 * h][v];
+                x1 = gamma * acc[2 * h + 1][v];
+            }
+            if (r + 1 < p.M && r + 1 < p.split) {
+                double *dst = p.D2 + j * p.ldd2 + r;
+                if (p.d2_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
+                else { dst[0] = x0; dst[1] = x1; }
+            } else if (r + 1 < p.M && r >= p.split) {
+                double *dst = p.D + j * p.ldd + r;
+                if (p.d_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
+                else { dst[0] = x0; dst[1] = x1; }
+            } else {
+                if (r < p.split) p.D2[r + j * p.ldd2] = x0;
+                else p.D[r + j * p.ldd] = x0;
+                if (r + 1 < p.M) {
+                    if (r + 1 < p.split) p.D2[r + 1 + j * p.ldd2] = x1;
+                    else p.D[r + 1 + j * p.ldd] = x1;
+                }
+            }
+        }
+    }
+}
+
 // ---- fp32 products without LDS ---------------------------------------------
 // The same structure for fp32 on v_mfma_f32_16x16x4f32 (32 cycles: twice the
 // fp64 rate on half the operand bytes, so the same operand traffic per
@@ -1132,18 +1297,17 @@ hipError_t launch_lf(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Complex fp64 single products on gemm_lf_kernel through the real view.
-hipError_t launch_lf_cplx(const GemmDesc &g, hipStream_t st) {
-    GemmParams<cplx> pc;
-    dim3 grid;
-    hipError_t e = tile_params<cplx, 128, 128>(g, pc, grid);
-    if (e != hipSuccess || grid.x == 0) return e;
+// The real view of a complex fp64 product for the LDS-free kernels: M and
+// K doubled (real rows and k), Bm, C, D and D2 read as interleaved real with
+// doubled leading dimensions, A kept in complex addressing (lda in complex
+// elements, extA in doubles).
+GemmParams<double> real_view(const GemmParams<cplx> &pc) {
     GemmParams<double> p{};
     p.M = 2 * pc.M;
     p.N = pc.N;
     p.K = 2 * pc.K;
     p.A = reinterpret_cast<const double *>(pc.A);
-    p.lda = pc.lda;  // complex elements (A keeps complex addressing)
+    p.lda = pc.lda;
     p.extA = 2 * pc.extA;
     p.Bm = reinterpret_cast<const double *>(pc.Bm);
     p.ldb = 2 * pc.ldb;
@@ -1163,12 +1327,80 @@ hipError_t launch_lf_cplx(const GemmDesc &g, hipStream_t st) {
     p.c_vec = pc.c_vec;
     p.d_vec = pc.d_vec;
     p.d2_vec = pc.d2_vec;
+    p.binner = 1;
+    return p;
+}
+
+// Complex fp64 single products on gemm_lf_kernel through the real view.
+hipError_t launch_lf_cplx(const GemmDesc &g, hipStream_t st) {
+    GemmParams<cplx> pc;
+    dim3 grid;
+    hipError_t e = tile_params<cplx, 128, 128>(g, pc, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    GemmParams<double> p = real_view(pc);
     p.tilesM = (int)((p.M + 127) / 128);
     p.tilesN = (int)((p.N + 127) / 128);
-    p.binner = 1;
     grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
     hipLaunchKernelGGL((gemm_lf_kernel<3, 4, false, true>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
+}
+
+// fp64 and complex fp64 products that split-K would cut, on gemm_ks_kernel:
+// 64 x 16 tiles, KW = the split-K factor (at most 8) waves on each.
+template <int KW>
+hipError_t launch_ks_kw(const GemmParams<double> &p, bool tri, bool cplx_view, hipStream_t st) {
+    const dim3 grid((unsigned)(p.tilesM * p.tilesN), 1u);
+    const dim3 block(64 * KW);
+    if (tri && cplx_view) hipLaunchKernelGGL((gemm_ks_kernel<3, KW, true, true>), grid, block, 0, st, p);
+    else if (tri) hipLaunchKernelGGL((gemm_ks_kernel<3, KW, true, false>), grid, block, 0, st, p);
+    else if (cplx_view) hipLaunchKernelGGL((gemm_ks_kernel<3, KW, false, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((gemm_ks_kernel<3, KW, false, false>), grid, block, 0, st, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_ks(int dtype, const GemmDesc &g, int parts, hipStream_t st) {
+    GemmParams<double> p;
+    dim3 grid;
+    hipError_t e;
+    if (dtype == C64F) {
+        GemmParams<cplx> pc;
+        e = tile_params<cplx, 64, 16>(g, pc, grid);
+        if (e != hipSuccess || grid.x == 0) return e;
+        p = real_view(pc);
+    } else {
+        e = tile_params<double, 64, 16>(g, p, grid);
+        if (e != hipSuccess || grid.x == 0) return e;
+    }
+    const int64_t tM = (p.M + 63) / 64, tN = (p.N + 15) / 16;
+    if (tM * tN > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    p.tilesM = (int)tM;
+    p.tilesN = (int)tN;
+    const bool tri = g.a_lower != 0, cv = dtype == C64F;
+    if (parts >= 8) return launch_ks_kw<8>(p, tri, cv, st);
+    if (parts >= 4) return launch_ks_kw<4>(p, tri, cv, st);
+    return launch_ks_kw<2>(p, tri, cv, st);
+}
+
+// Whether a split-K product runs on gemm_ks_kernel: fp64 or complex fp64, a
+// single product with K a multiple of 8 (split K is always a multiple of
+// 256) and 16-byte aligned A and Bm whose tiles stay within 32-bit buffer
+// offsets (as gemm_launch's non-wide path), with at least 256 output tiles
+// of 64 x 16 real rows x columns: with fewer the workgroups are too few to
+// hide their latency, and the batched partial products measured faster
+// (fp64 8192 x 64, IB 1024: 0.418 ms against 0.441; 8192 x 256: 0.697
+// against 0.618 in favour of this form).  TRSM_GEMM_KS=0 keeps the batched
+// partial products, =1 takes this form whatever the tile count (tuning and
+// tests).
+bool use_ks(int dtype, const GemmDesc &g) {
+    if (dtype != R64F && dtype != C64F) return false;
+    const char *e = std::getenv("TRSM_GEMM_KS");
+    if ((e && e[0] == '0') || !use_gemm_lf()) return false;
+    const int64_t Mr = dtype == C64F ? 2 * g.M : g.M;
+    if (!(e && e[0] == '1') && ((Mr + 63) / 64) * ((g.N + 15) / 16) < 256) return false;
+    const int64_t es = (int64_t)dtype_size(dtype);
+    if (g.batch > 1 || g.b_lower || g.M <= 0 || g.N <= 0 || g.K % 8 != 0) return false;
+    if (g.lda > (0x7fffffffLL - 4096) / (es * 32) || g.ldb > (0x7fffffffLL - 4096) / (es * 128)) return false;
+    return aligned16(g.A, g.lda, es) && aligned16(g.Bm, g.ldb, es);
 }
 
 // Triangular fp64 product (the diagonal-block solve): workgroups of four
@@ -1379,6 +1611,7 @@ int gemm_splitk_parts(int dtype, int64_t M, int64_t N, int64_t K, int64_t target
 hipError_t gemm_splitk_launch(int dtype, const GemmDesc &g, int parts, void *partial,
                               hipStream_t stream) {
     if (parts <= 1) return gemm_launch(dtype, g, stream);
+    if (use_ks(dtype, g)) return launch_ks(dtype, g, parts, stream);
     if (g.M <= 0 || g.N <= 0) return hipSuccess;
     if (g.batch > 1 || g.K % parts != 0 || partial == nullptr ||
         (int64_t)parts * g.M * g.N > kSplitKMaxElems)
