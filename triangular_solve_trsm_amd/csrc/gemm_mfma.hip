@@ -739,15 +739,22 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
         const int64_t nkf = K / 8;  // full chunks
 #pragma unroll
         for (int u = 0; u < RING; ++u) load(u, 8 * u, u < nkf);
-        for (int64_t kc = 0; kc < nkf; kc += RING) {
+        // Whole rounds of RING chunks with no condition around the products
+        // and loads, then the last chunks (already loaded): a condition per
+        // slot in the loop gave the wait counters a path on which the later
+        // slots' loads were not issued, and the loop head then waited for
+        // every load in flight once per round.
+        int64_t kc = 0;
+        for (; kc + RING <= nkf; kc += RING) {
 #pragma unroll
             for (int u = 0; u < RING; ++u) {
-                if (kc + u < nkf) {  // uniform
-                    compute(ra[u], rb[u]);
-                    load(u, 8 * (kc + u + RING), kc + u + RING < nkf);
-                }
+                compute(ra[u], rb[u]);
+                load(u, 8 * (kc + u + RING), kc + u + RING < nkf);
             }
         }
+#pragma unroll
+        for (int u = 0; u < RING; ++u)
+            if (kc + u < nkf) compute(ra[u], rb[u]);  // uniform
         // ragged last chunk: k = 8 nkf + 2q + s exists only while below K; the
         // lanes past it read zero from A and Bm (8-byte Bm loads, so a pair
         // straddling K keeps its first element)
@@ -941,15 +948,18 @@ __global__ __launch_bounds__(64 * KW) void gemm_ks_kernel(GemmParams<double> p) 
     };
 #pragma unroll
     for (int u = 0; u < RING; ++u) load(u, kc0 + u, kc0 + u < kfe);
-    for (int64_t kc = kc0; kc < kfe; kc += RING) {
+    // whole rounds, then the last chunks (as gemm_lf_kernel)
+    int64_t kc = kc0;
+    for (; kc + RING <= kfe; kc += RING) {
 #pragma unroll
         for (int u = 0; u < RING; ++u) {
-            if (kc + u < kfe) {  // uniform
-                compute(ra[u], rb[u]);
-                load(u, kc + u + RING, kc + u + RING < kfe);
-            }
+            compute(ra[u], rb[u]);
+            load(u, kc + u + RING, kc + u + RING < kfe);
         }
     }
+#pragma unroll
+    for (int u = 0; u < RING; ++u)
+        if (kc + u < kfe) compute(ra[u], rb[u]);  // uniform
     // ---- the waves' sums into wave 0, in wave order ------------------------
     if (wave > 0) {
 #pragma unroll
@@ -1084,15 +1094,18 @@ __global__ __launch_bounds__(256, 1) void gemm_lf32_kernel(GemmParams<float> p) 
         const int64_t nkf = K / 16;  // full chunks
 #pragma unroll
         for (int u = 0; u < RING; ++u) load(u, 16 * u, u < nkf);
-        for (int64_t kc = 0; kc < nkf; kc += RING) {
+        // whole rounds, then the last chunks (as gemm_lf_kernel)
+        int64_t kc = 0;
+        for (; kc + RING <= nkf; kc += RING) {
 #pragma unroll
             for (int u = 0; u < RING; ++u) {
-                if (kc + u < nkf) {  // uniform
-                    compute(ra[u], rb[u]);
-                    load(u, 16 * (kc + u + RING), kc + u + RING < nkf);
-                }
+                compute(ra[u], rb[u]);
+                load(u, 16 * (kc + u + RING), kc + u + RING < nkf);
             }
         }
+#pragma unroll
+        for (int u = 0; u < RING; ++u)
+            if (kc + u < nkf) compute(ra[u], rb[u]);  // uniform
         const int kr = (int)(K - 16 * nkf);
         if (kr > 0) {
             const int64_t k0 = 16 * nkf;
