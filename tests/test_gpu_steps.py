@@ -155,6 +155,32 @@ def test_gemm_lds_free_edges(T, dtype, case, lf, monkeypatch):
               split=split)
 
 
+@pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("case", LF_CASES)
+def test_gemm_lds_free_f32_256_tiles(T, case, lf, monkeypatch):
+    """fp32 products with 256 to 511 workgroups of 128 x 128 (here 8 x 32 =
+    256) take the LDS-free kernel with a ring of three chunks (the ring of
+    five above 512): the same edge cases as above on half the rows."""
+    monkeypatch.setenv("TRSM_GEMM_LF", lf)
+    M, N, K, ldpad, split, beta, gamma = case
+    M = M // 2
+    pa = ldpad + (-(M + ldpad)) % 4
+    pb = ldpad + (-(K + ldpad)) % 4
+    gemm_case(T, "f32", M, N, K, beta, gamma, seed=K + M + 1, ldpad=ldpad, ldpad_a=pa, ldpad_b=pb,
+              split=min(split, M))
+
+
+@pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("M,N", [(1000, 4000), (960, 4096), (1023, 4000), (1024, 3970)])
+def test_gemm_lds_free_triangular_f32_256(T, M, N, lf, monkeypatch):
+    """Triangular fp32 products with 256 folded workgroups (8 pairs of row
+    tiles x 32 column blocks) on the ring of three: ragged last row tile, an
+    odd tile count, odd M, ragged N."""
+    monkeypatch.setenv("TRSM_GEMM_LF", lf)
+    pa = (-M) % 4
+    gemm_case(T, "f32", M, N, M, 0.0, -0.75, seed=M + N + 1, a_lower=True, ldpad_a=pa, ldpad_b=pa)
+
+
 LF_CPLX_CASES = [
     # (M, N, K, ldpad, split, beta, gamma) in complex elements: the real view
     # 2M x N gives 16 x 32 = 512 tiles of 128 x 128

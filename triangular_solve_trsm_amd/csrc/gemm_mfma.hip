@@ -1499,18 +1499,28 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
         if (g.batch <= 1 && !g.b_lower) {
             const bool lf = use_gemm_lf() && aligned16(g.A, g.lda, 4) && aligned16(g.Bm, g.ldb, 4);
             const int64_t tN128 = (g.N + 127) / 128;
+            // 512 or more workgroups of 128 columns: a ring of five chunks;
+            // 256 to 511 (fp32 4096^2: 1024 x 4096 products) in rounds of 256
+            // more than 3/4 full: a ring of three, whose smaller register set
+            // leaves room for two waves per SIMD.  Measured: 4096^2 0.680 ->
+            // 0.661 ms against the LDS tiles; the ring of three lost on
+            // 8192^2 (4.43 -> 5.17 ms) and on 384 workgroups (an update of
+            // fp32 8192 x 2048: 144 -> 183 us, half the CUs running a second
+            // round alone)
             if (g.a_lower) {
                 const int64_t pairs = ((g.M + 63) / 64 + 1) / 2;
                 if (lf && pairs * tN128 >= 512) return launch_lf32<5, 2, true>(g, st);
+                const int64_t p128 = pairs * tN128;
+                if (lf && p128 >= 256 && 4 * p128 > 3 * 256 * ((p128 + 255) / 256)) return launch_lf32<3, 2, true>(g, st);
                 // fewer workgroups: the LDS tile, 64 x 64 while that still
-                // gives 512 folded workgroups (fp32 4096^2: the 1024 x 4096
-                // solve 48.5 -> 46 us against 64 x 32, the whole solve 0.706
-                // -> 0.694 ms)
+                // gives 512 folded workgroups
                 if (pairs * ((g.N + 63) / 64) >= 512) return launch_tile<T, 64, 64, KT>(g, st);
             } else if (lf) {
                 const int64_t t128 = ((g.M + 127) / 128) * tN128;
                 if (g.M > 64 && t128 >= 512 && 4 * t128 >= 3 * 512 * ((t128 + 511) / 512))
                     return launch_lf32<5, 4, false>(g, st);
+                if (g.M > 64 && t128 >= 256 && t128 < 512 && 4 * t128 > 3 * 256 * ((t128 + 255) / 256))
+                    return launch_lf32<3, 4, false>(g, st);
             }
         }
     }
