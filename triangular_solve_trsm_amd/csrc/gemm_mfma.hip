@@ -1025,9 +1025,10 @@ __global__ __launch_bounds__(64 * KW) void gemm_ks_kernel(GemmParams<double> p) 
 //     16-byte quadruples;
 //   * the ragged last chunk zeroes the lanes whose k is past K, with 4-byte
 //     Bm loads there.
-// NBT and TRI as for gemm_lf_kernel.
-template <int RING, int NBT, bool TRI>
-__global__ __launch_bounds__(256, 1) void gemm_lf32_kernel(GemmParams<float> p) {
+// NBT and TRI as for gemm_lf_kernel; MINB: workgroups per CU the register
+// budget is sized for.
+template <int RING, int NBT, bool TRI, int MINB = 1>
+__global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1437,7 +1438,7 @@ hipError_t launch_lf_tri(const GemmDesc &g, hipStream_t st) {
 
 // fp32 single products on gemm_lf32_kernel: the update tile 128 x 128
 // (64 x 64 per wave), the triangular product's wave tile 64 x 32.
-template <int RING, int NBT, bool TRI>
+template <int RING, int NBT, bool TRI, int MINB = 1>
 hipError_t launch_lf32(const GemmDesc &g, hipStream_t st) {
     GemmParams<float> p;
     dim3 grid;
@@ -1451,7 +1452,7 @@ hipError_t launch_lf32(const GemmDesc &g, hipStream_t st) {
         p.tilesN = (int)((g.N + 32 * NBT - 1) / (32 * NBT));
     }
     grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
-    hipLaunchKernelGGL((gemm_lf32_kernel<RING, NBT, TRI>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_lf32_kernel<RING, NBT, TRI, MINB>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1511,7 +1512,10 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
                 const int64_t pairs = ((g.M + 63) / 64 + 1) / 2;
                 if (lf && pairs * tN128 >= 512) return launch_lf32<5, 2, true>(g, st);
                 const int64_t p128 = pairs * tN128;
-                if (lf && p128 >= 256 && 4 * p128 > 3 * 256 * ((p128 + 255) / 256)) return launch_lf32<3, 2, true>(g, st);
+                // (the triangular form there with 64 x 16 wave tiles: twice the
+                // workgroups, two per CU; 0.659 -> 0.652 ms on 4096^2)
+                if (lf && p128 >= 256 && 4 * p128 > 3 * 256 * ((p128 + 255) / 256))
+                    return launch_lf32<3, 1, true, 2>(g, st);
                 // fewer workgroups: the LDS tile, 64 x 64 while that still
                 // gives 512 folded workgroups
                 if (pairs * ((g.N + 63) / 64) >= 512) return launch_tile<T, 64, 64, KT>(g, st);
