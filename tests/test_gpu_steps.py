@@ -256,8 +256,21 @@ def test_gemm_k_zero_and_gamma_zero(T, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64", "c32"])
 @pytest.mark.parametrize("ib", [64, 128, 256, 512, 1024])
 def test_diag_inv_vs_oracle_identity_solve(T, dtype, ib):
+    diag_inv_case(T, dtype, ib, ib * 2 + 37)  # two full blocks and a ragged one
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+@pytest.mark.parametrize("ib,m", [(256, 3 * 256 + 200), (512, 2 * 512 + 300), (1024, 3 * 1024), (1024, 2048 + 777)])
+def test_diag_inv_doubling_pairs(T, dtype, ib, m):
+    """Batched doubling products over several parent blocks: full pairs in
+    every block, a last block with no ragged rows, and ragged last blocks
+    whose last pair is cut short at different levels."""
+    print(f"case {dtype} ib={ib} m={m}", flush=True)
+    diag_inv_case(T, dtype, ib, m)
+
+
+def diag_inv_case(T, dtype, ib, m):
     import torch
-    m = ib * 2 + 37  # two full blocks and a ragged one
     L, _ = make_problem(dtype, m, 1, seed=ib)
     nb = (m + ib - 1) // ib
     W = torch.full((nb * ib * ib,), float("nan"), dtype={"f32": torch.float32, "f64": torch.float64,

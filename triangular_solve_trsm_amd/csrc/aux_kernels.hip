@@ -3,6 +3,10 @@
 // panel buffer that the first diagonal-block solve reads, and the index
 // reflections that bring the other TRSM variants to the left-lower form.
 #include "scalar_ops.h"
+#include "buffer_ops.h"
+
+#include <cstdint>
+#include <type_traits>
 
 namespace trsm {
 namespace {
@@ -22,16 +26,37 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(int64_t m, int64_t n, T 
     }
 }
 
-template <typename T>
+// dst(i, j) = src(i, j) for a rows x n column-major panel.  Thread t of a
+// workgroup takes V consecutive rows (one 16-byte access when VEC, else one
+// element) of column t / tpc, with tpc threads per column (64, 128 or 256,
+// the fewest that cover the rows in one pass where possible), so a short
+// panel still keeps every lane busy.  Each thread copies CW columns
+// cpw = 256 / tpc apart, all loads before the stores, and the workgroups
+// stride over the column groups.  No 64-bit division per element.
+template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void copy_panel_kernel(int64_t rows, int64_t n,
                                                          const T *__restrict__ src, int64_t lds,
-                                                         T *__restrict__ dst, int64_t ldd) {
-    const int64_t total = rows * n;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t i = e % rows;
-        const int64_t j = e / rows;
-        dst[i + j * ldd] = src[i + j * lds];
+                                                         T *__restrict__ dst, int64_t ldd, int tpc) {
+    using W = typename std::conditional<VEC, u4v, T>::type;
+    constexpr int V = (int)(sizeof(W) / sizeof(T));
+    constexpr int CW = 4;
+    const int t = threadIdx.x;
+    const int cpw = 256 / tpc;
+    const int64_t i = ((int64_t)blockIdx.x * tpc + (t % tpc)) * V;
+    if (i >= rows) return;
+    const int64_t group = (int64_t)cpw * CW;  // columns per workgroup and pass
+    for (int64_t j0 = (int64_t)blockIdx.y * group + t / tpc; j0 < n; j0 += (int64_t)gridDim.y * group) {
+        W v[CW];
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+            const int64_t j = j0 + (int64_t)c * cpw;
+            if (j < n) v[c] = *reinterpret_cast<const W *>(src + i + j * lds);
+        }
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+            const int64_t j = j0 + (int64_t)c * cpw;
+            if (j < n) *reinterpret_cast<W *>(dst + i + j * ldd) = v[c];
+        }
     }
 }
 
@@ -112,10 +137,24 @@ hipError_t fill_t(int64_t m, int64_t n, void *B, int64_t ldb, int64_t sB, int64_
 template <typename T>
 hipError_t copy_t(int64_t rows, int64_t n, const void *src, int64_t lds, void *dst, int64_t ldd,
                   hipStream_t st) {
-    const int64_t total = rows * n;
-    if (total <= 0) return hipSuccess;
-    hipLaunchKernelGGL((copy_panel_kernel<T>), dim3(grid_for(total)), dim3(256), 0, st, rows, n,
-                       static_cast<const T *>(src), lds, static_cast<T *>(dst), ldd);
+    if (rows <= 0 || n <= 0) return hipSuccess;
+    constexpr int64_t V = 16 / (int64_t)sizeof(T);
+    const bool vec = V > 1 && rows % V == 0 && lds % V == 0 && ldd % V == 0 &&
+                     reinterpret_cast<uintptr_t>(src) % 16 == 0 && reinterpret_cast<uintptr_t>(dst) % 16 == 0;
+    const int64_t per = vec ? (rows + V - 1) / V : rows;  // threads per column
+    const int tpc = per <= 64 ? 64 : per <= 128 ? 128 : 256;
+    const int64_t gx = (per + tpc - 1) / tpc;
+    const int64_t group = (256 / tpc) * 4;
+    int64_t gy = (n + group - 1) / group;
+    if (gy > 65535) gy = 65535;  // the kernel strides over the rest
+    if (gx > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)gx, (unsigned)gy);
+    if (vec)
+        hipLaunchKernelGGL((copy_panel_kernel<T, true>), grid, dim3(256), 0, st, rows, n,
+                           static_cast<const T *>(src), lds, static_cast<T *>(dst), ldd, tpc);
+    else
+        hipLaunchKernelGGL((copy_panel_kernel<T, false>), grid, dim3(256), 0, st, rows, n,
+                           static_cast<const T *>(src), lds, static_cast<T *>(dst), ldd, tpc);
     return hipGetLastError();
 }
 
