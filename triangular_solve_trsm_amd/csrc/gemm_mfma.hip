@@ -632,7 +632,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams<T> p) {
 // the whole 2 x 2 block it feeds for complex row i: (ar, ai) on step s = 0,
 // (-ai, ar) on s = 1; a pair of output rows is one complex element, so C is
 // scaled by sc and the result by gamma as complex numbers.
-template <int RING, int NBT, bool TRI, bool CPLX = false>
+// BAT: batched launches, problem blockIdx.y (as gemm_kernel).  BLO: Bm is
+// lower triangular with explicit zeros above its diagonal (the inversion's
+// second product): a wave's K loop starts at its first column.
+template <int RING, int NBT, bool TRI, bool CPLX = false, bool BAT = false, bool BLO = false>
 __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -643,8 +646,19 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
     const int q = lane >> 4;
     int tm, tn;
     map_tile(blockIdx.x, p.tilesM, p.tilesN, tm, tn);
-    const double *__restrict__ pA = p.A;
-    const double *__restrict__ pB = p.Bm;
+    const int zo = BAT ? (int)blockIdx.y / p.binner : 0;
+    const int zi = BAT ? (int)blockIdx.y - zo * p.binner : 0;
+    const double *__restrict__ pA = p.A + (zo * p.sAo + zi * p.sAi);
+    const double *__restrict__ pB = p.Bm + (zo * p.sBo + zi * p.sBi);
+    // C, D and D2 of the problem, formed where they are used
+    auto cptr = [&]() -> const double * {
+        if constexpr (BAT) return p.C + (zo * p.sCo + zi * p.sCi);
+        else return p.C;
+    };
+    auto dptr = [&](double *base) -> double * {
+        if constexpr (BAT) return base + (zo * p.sDo + zi * p.sDi);
+        else return base;
+    };
     const int64_t lda = p.lda, ldb = p.ldb;
     // real: rows 2c, 2c + 1 at k = 2q (offA0) and 2q + 1 (offA1), 32 rows
     // further at +256 bytes; complex: element (c, q) and 16 complex rows
@@ -658,8 +672,8 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
     const double sci = p.sc.im, gammai = p.gamma.im;  // complex only
 
     // the wave's output block: rows [r0, r0 + 64), columns [c0, c0 + 16 NBT),
-    // products over k in [0, K)
-    auto run_tile = [&](const int64_t r0, const int64_t c0, const int64_t K) {
+    // products over k in [kb, K) (kb a multiple of 8)
+    auto run_tile = [&](const int64_t r0, const int64_t c0, const int64_t kb, const int64_t K) {
         // ---- accumulators start at sc * C ------------------------------------
         d4 acc[4][NBT];
 #pragma unroll
@@ -670,7 +684,7 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
                 const int64_t rr = r0 + 2 * (q + 4 * v);
                 double x[4] = {0.0, 0.0, 0.0, 0.0};
                 if (p.has_c && j < p.N) {
-                    const double *col = p.C + j * p.ldc;
+                    const double *col = cptr() + j * p.ldc;
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {  // rows rr (tiles 0, 1) and rr + 32 (tiles 2, 3)
                         const int64_t r = rr + 32 * h;
@@ -736,9 +750,9 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
                         acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bq[b][s], acc[a][b], 0, 0, 0);
             }
         };
-        const int64_t nkf = K / 8;  // full chunks
+        const int64_t nkf = (K - kb) / 8;  // full chunks
 #pragma unroll
-        for (int u = 0; u < RING; ++u) load(u, 8 * u, u < nkf);
+        for (int u = 0; u < RING; ++u) load(u, kb + 8 * u, u < nkf);
         // Whole rounds of RING chunks with no condition around the products
         // and loads, then the last chunks (already loaded): a condition per
         // slot in the loop gave the wait counters a path on which the later
@@ -749,7 +763,7 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
 #pragma unroll
             for (int u = 0; u < RING; ++u) {
                 compute(ra[u], rb[u]);
-                load(u, 8 * (kc + u + RING), kc + u + RING < nkf);
+                load(u, kb + 8 * (kc + u + RING), kc + u + RING < nkf);
             }
         }
 #pragma unroll
@@ -758,9 +772,9 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
         // ragged last chunk: k = 8 nkf + 2q + s exists only while below K; the
         // lanes past it read zero from A and Bm (8-byte Bm loads, so a pair
         // straddling K keeps its first element)
-        const int kr = (int)(K - 8 * nkf);
+        const int kr = (int)(K - kb - 8 * nkf);
         if (kr > 0) {
-            const int64_t k0 = 8 * nkf;
+            const int64_t k0 = kb + 8 * nkf;
             const int64_t oa = r0 + k0 * lda;
             const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, (p.extA - oa) * 8);
             const uint32_t dead = 0xfffffff0u;
@@ -807,19 +821,19 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
                         x1 = gamma * acc[2 * h + 1][b][v];
                     }
                     if (r + 1 < p.M && r + 1 < p.split) {
-                        double *dst = p.D2 + j * p.ldd2 + r;
+                        double *dst = dptr(p.D2) + j * p.ldd2 + r;
                         if (p.d2_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
                         else { dst[0] = x0; dst[1] = x1; }
                     } else if (r + 1 < p.M && r >= p.split) {
-                        double *dst = p.D + j * p.ldd + r;
+                        double *dst = dptr(p.D) + j * p.ldd + r;
                         if (p.d_vec) *reinterpret_cast<d2v *>(dst) = d2v{x0, x1};
                         else { dst[0] = x0; dst[1] = x1; }
                     } else {
-                        if (r < p.split) p.D2[r + j * p.ldd2] = x0;
-                        else p.D[r + j * p.ldd] = x0;
+                        if (r < p.split) dptr(p.D2)[r + j * p.ldd2] = x0;
+                        else dptr(p.D)[r + j * p.ldd] = x0;
                         if (r + 1 < p.M) {
-                            if (r + 1 < p.split) p.D2[r + 1 + j * p.ldd2] = x1;
-                            else p.D[r + 1 + j * p.ldd] = x1;
+                            if (r + 1 < p.split) dptr(p.D2)[r + 1 + j * p.ldd2] = x1;
+                            else dptr(p.D)[r + 1 + j * p.ldd] = x1;
                         }
                     }
                 }
@@ -834,12 +848,13 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
         const int t1 = T - 1 - tm;
         for (int pass = 0; pass < (t1 != tm ? 2 : 1); ++pass) {
             const int64_t r0 = (int64_t)(pass == 0 ? tm : t1) * 64;
-            run_tile(r0, c0, r0 + 64 < p.K ? r0 + 64 : p.K);
+            run_tile(r0, c0, 0, r0 + 64 < p.K ? r0 + 64 : p.K);
         }
     } else {
         const int64_t r0 = (int64_t)tm * 128 + (wave & 1) * 64;
         const int64_t c0 = (int64_t)tn * 32 * NBT + (int64_t)(wave >> 1) * 16 * NBT;
-        run_tile(r0, c0, p.K);
+        // lower-triangular Bm: its rows above c0 are zero in these columns
+        run_tile(r0, c0, BLO ? (c0 < p.K ? c0 : p.K) : 0, p.K);
     }
 }
 
@@ -1311,6 +1326,50 @@ hipError_t launch_lf(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// The diagonal inversion's batched fp64 products on gemm_lf_kernel, 64 x 16
+// per wave: the triangular first product folds row tiles (four waves side by
+// side on 64 columns), the second (triangular Bm) runs 128 x 32 workgroups
+// whose waves start K at their first column.  Taken from 256 workgroups
+// (TRSM_INV_LF_MIN overrides; TRSM_INV_LF=0 keeps the LDS tile): with fewer,
+// one wave per SIMD at most cannot hide its loads.  Measured (whole solves,
+// three rounds on one box): fp64 8192 x 64 0.419 -> 0.411 ms, 8192 x 256
+// 0.599 -> 0.593 ms, 4096^2 and 8192^2 unchanged within noise; taken for
+// every level it lost (4096^2 inversion 133 -> 145 us).
+bool use_inv_lf(const GemmDesc &g) {
+    const char *e = std::getenv("TRSM_INV_LF");
+    if ((e && e[0] == '0') || !use_gemm_lf() || g.split != 0 || g.D2 != nullptr) return false;
+    const auto al = [](int64_t o, int64_t i) { return (o * 8) % 16 == 0 && (i * 8) % 16 == 0; };
+    if (!(aligned16(g.A, g.lda, 8) && aligned16(g.Bm, g.ldb, 8) && al(g.sAo, g.sAi) && al(g.sBo, g.sBi)))
+        return false;
+    const int64_t wg = g.batch * (g.a_lower ? (((g.M + 63) / 64 + 1) / 2) * ((g.N + 63) / 64)
+                                            : ((g.M + 127) / 128) * ((g.N + 31) / 32));
+    const char *m = std::getenv("TRSM_INV_LF_MIN");
+    return wg >= (m ? std::atoll(m) : 256);
+}
+
+template <int RING>
+hipError_t launch_lf_batched(const GemmDesc &g, hipStream_t st) {
+    GemmParams<double> p;
+    dim3 grid;
+    hipError_t e = tile_params<double, 128, 128>(g, p, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    if (g.a_lower) {
+        p.tilesM = (int)(((g.M + 63) / 64 + 1) / 2);  // row-tile pairs
+        p.tilesN = (int)((g.N + 63) / 64);
+        grid = dim3((unsigned)(p.tilesM * p.tilesN), grid.y);
+        hipLaunchKernelGGL((gemm_lf_kernel<RING, 1, true, false, true, false>), grid, dim3(256), 0, st, p);
+    } else {
+        p.tilesM = (int)((g.M + 127) / 128);
+        p.tilesN = (int)((g.N + 31) / 32);
+        grid = dim3((unsigned)(p.tilesM * p.tilesN), grid.y);
+        if (g.b_lower)
+            hipLaunchKernelGGL((gemm_lf_kernel<RING, 1, false, false, true, true>), grid, dim3(256), 0, st, p);
+        else
+            hipLaunchKernelGGL((gemm_lf_kernel<RING, 1, false, false, true, false>), grid, dim3(256), 0, st, p);
+    }
+    return hipGetLastError();
+}
+
 // The real view of a complex fp64 product for the LDS-free kernels: M and
 // K doubled (real rows and k), Bm, C, D and D2 read as interleaved real with
 // doubled leading dimensions, A kept in complex addressing (lda in complex
@@ -1486,6 +1545,9 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
     if (g.batch > 1 && (g.b_lower || (g.a_lower && g.sKo == 0))) {
         if constexpr (std::is_same<T, float>::value) return launch_tile<T, 32, 32, KT>(g, st);
         if constexpr (std::is_same<T, cplx>::value) return launch_tile<T, 64, 64, KT>(g, st);
+        if constexpr (std::is_same<T, double>::value) {
+            if (use_inv_lf(g)) return launch_lf_batched<4>(g, st);
+        }
     }
     // Triangular solve products (folded pairs of row tiles) with enough work
     // for 512 workgroups on a wider tile: 64 x 128 for fp64, 64 x 64 for
