@@ -259,14 +259,15 @@ def test_diag_inv_vs_oracle_identity_solve(T, dtype, ib):
     diag_inv_case(T, dtype, ib, ib * 2 + 37)  # two full blocks and a ragged one
 
 
-@pytest.mark.parametrize("dtype,lf", [("f32", None), ("f64", "1"), ("f64", "0")])
+@pytest.mark.parametrize("dtype,lf", [("f32", None), ("f64", "1"), ("f64", "0"), ("c64", "1"), ("c64", "0")])
 @pytest.mark.parametrize("ib,m", [(256, 3 * 256 + 200), (512, 2 * 512 + 300), (1024, 3 * 1024), (1024, 2048 + 777)])
 def test_diag_inv_doubling_pairs(T, dtype, ib, m, lf, monkeypatch):
     """Batched doubling products over several parent blocks: full pairs in
     every block, a last block with no ragged rows, and ragged last blocks
-    whose last pair is cut short at different levels.  fp64 runs every
-    level's products on the LDS-free kernel (TRSM_INV_LF_MIN=1) and on the
-    LDS tile (TRSM_INV_LF=0)."""
+    whose last pair is cut short at different levels.  fp64 and complex
+    fp64 run every level's products on the LDS-free kernel
+    (TRSM_INV_LF_MIN=1; complex through the real view) and on the LDS tile
+    (TRSM_INV_LF=0)."""
     if lf == "1":
         monkeypatch.setenv("TRSM_INV_LF_MIN", "1")
     elif lf == "0":

@@ -854,7 +854,9 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
         const int64_t r0 = (int64_t)tm * 128 + (wave & 1) * 64;
         const int64_t c0 = (int64_t)tn * 32 * NBT + (int64_t)(wave >> 1) * 16 * NBT;
         // lower-triangular Bm: its rows above c0 are zero in these columns
-        run_tile(r0, c0, BLO ? (c0 < p.K ? c0 : p.K) : 0, p.K);
+        // (complex: real k 2j starts complex column j)
+        const int64_t kb = (CPLX ? 2 : 1) * c0;
+        run_tile(r0, c0, BLO ? (kb < p.K ? kb : p.K) : 0, p.K);
     }
 }
 
@@ -1335,14 +1337,15 @@ hipError_t launch_lf(const GemmDesc &g, hipStream_t st) {
 // three rounds on one box): fp64 8192 x 64 0.419 -> 0.411 ms, 8192 x 256
 // 0.599 -> 0.593 ms, 4096^2 and 8192^2 unchanged within noise; taken for
 // every level it lost (4096^2 inversion 133 -> 145 us).
-bool use_inv_lf(const GemmDesc &g) {
+bool use_inv_lf(const GemmDesc &g, size_t es) {
     const char *e = std::getenv("TRSM_INV_LF");
     if ((e && e[0] == '0') || !use_gemm_lf() || g.split != 0 || g.D2 != nullptr) return false;
-    const auto al = [](int64_t o, int64_t i) { return (o * 8) % 16 == 0 && (i * 8) % 16 == 0; };
-    if (!(aligned16(g.A, g.lda, 8) && aligned16(g.Bm, g.ldb, 8) && al(g.sAo, g.sAi) && al(g.sBo, g.sBi)))
+    const auto al = [&](int64_t o, int64_t i) { return (o * (int64_t)es) % 16 == 0 && (i * (int64_t)es) % 16 == 0; };
+    if (!(aligned16(g.A, g.lda, es) && aligned16(g.Bm, g.ldb, es) && al(g.sAo, g.sAi) && al(g.sBo, g.sBi)))
         return false;
-    const int64_t wg = g.batch * (g.a_lower ? (((g.M + 63) / 64 + 1) / 2) * ((g.N + 63) / 64)
-                                            : ((g.M + 127) / 128) * ((g.N + 31) / 32));
+    const int64_t Mr = es == 16 ? 2 * g.M : g.M;  // real rows (complex: the real view)
+    const int64_t wg = g.batch * (g.a_lower ? (((Mr + 63) / 64 + 1) / 2) * ((g.N + 63) / 64)
+                                            : ((Mr + 127) / 128) * ((g.N + 31) / 32));
     const char *m = std::getenv("TRSM_INV_LF_MIN");
     return wg >= (m ? std::atoll(m) : 256);
 }
@@ -1415,6 +1418,35 @@ hipError_t launch_lf_cplx(const GemmDesc &g, hipStream_t st) {
     p.tilesN = (int)((p.N + 127) / 128);
     grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
     hipLaunchKernelGGL((gemm_lf_kernel<3, 4, false, true>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+// The inversion's batched complex fp64 products on gemm_lf_kernel through
+// the real view (as launch_lf_batched; batch strides in doubles).
+template <int RING>
+hipError_t launch_lf_batched_cplx(const GemmDesc &g, hipStream_t st) {
+    GemmParams<cplx> pc;
+    dim3 grid;
+    hipError_t e = tile_params<cplx, 128, 128>(g, pc, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    GemmParams<double> p = real_view(pc);
+    p.binner = pc.binner;
+    p.sAo = 2 * pc.sAo; p.sAi = 2 * pc.sAi; p.sBo = 2 * pc.sBo; p.sBi = 2 * pc.sBi;
+    p.sCo = 2 * pc.sCo; p.sCi = 2 * pc.sCi; p.sDo = 2 * pc.sDo; p.sDi = 2 * pc.sDi;
+    if (g.a_lower) {
+        p.tilesM = (int)(((p.M + 63) / 64 + 1) / 2);  // real row-tile pairs
+        p.tilesN = (int)((p.N + 63) / 64);
+        grid = dim3((unsigned)(p.tilesM * p.tilesN), grid.y);
+        hipLaunchKernelGGL((gemm_lf_kernel<RING, 1, true, true, true, false>), grid, dim3(256), 0, st, p);
+    } else {
+        p.tilesM = (int)((p.M + 127) / 128);
+        p.tilesN = (int)((p.N + 31) / 32);
+        grid = dim3((unsigned)(p.tilesM * p.tilesN), grid.y);
+        if (g.b_lower)
+            hipLaunchKernelGGL((gemm_lf_kernel<RING, 1, false, true, true, true>), grid, dim3(256), 0, st, p);
+        else
+            hipLaunchKernelGGL((gemm_lf_kernel<RING, 1, false, true, true, false>), grid, dim3(256), 0, st, p);
+    }
     return hipGetLastError();
 }
 
@@ -1544,9 +1576,12 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
     // bitwise the same.
     if (g.batch > 1 && (g.b_lower || (g.a_lower && g.sKo == 0))) {
         if constexpr (std::is_same<T, float>::value) return launch_tile<T, 32, 32, KT>(g, st);
-        if constexpr (std::is_same<T, cplx>::value) return launch_tile<T, 64, 64, KT>(g, st);
+        if constexpr (std::is_same<T, cplx>::value) {
+            if (use_inv_lf(g, 16)) return launch_lf_batched_cplx<4>(g, st);
+            return launch_tile<T, 64, 64, KT>(g, st);
+        }
         if constexpr (std::is_same<T, double>::value) {
-            if (use_inv_lf(g)) return launch_lf_batched<4>(g, st);
+            if (use_inv_lf(g, 8)) return launch_lf_batched<4>(g, st);
         }
     }
     // Triangular solve products (folded pairs of row tiles) with enough work
