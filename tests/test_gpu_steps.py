@@ -181,6 +181,34 @@ def test_gemm_lds_free_triangular_f32_256(T, M, N, lf, monkeypatch):
     gemm_case(T, "f32", M, N, M, 0.0, -0.75, seed=M + N + 1, a_lower=True, ldpad_a=pa, ldpad_b=pa)
 
 
+@pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("M,N,beta,split,pad", [(1024, 4096, 0.0, 0, 0), (1000, 4000, 0.0, 0, 1),
+                                                (960, 4096, 1.5, 0, 0), (1023, 3999, -0.5, 130, 2)])
+def test_gemm_lds_free_triangular_f64_256(T, M, N, beta, split, pad, lf, monkeypatch):
+    """fp64 triangular products with 256 to 511 folded workgroups of 128
+    columns on the LDS-free ring of three (TRSM_GEMM_LF=0: the LDS tile):
+    ragged last row tile, odd tile count, odd M and N, a C term, rows
+    routed to D2 below a split inside a row pair."""
+    monkeypatch.setenv("TRSM_GEMM_LF", lf)
+    print(f"case f64 tri M={M} N={N} beta={beta} split={split} lf={lf}", flush=True)
+    gemm_case(T, "f64", M, N, M, beta, -0.75, seed=M + N + split, a_lower=True, split=split,
+              ldpad=pad, ldpad_a=pad, ldpad_b=pad)
+
+
+@pytest.mark.parametrize("form", ["1", "0"])
+@pytest.mark.parametrize("M,N,beta,split,pad", [(1024, 2048, 0.0, 0, 0), (1000, 2000, 0.0, 0, 1),
+                                                (999, 2048, 1.0 - 0.5j, 0, 0), (1024, 2047, 0.5, 130, 2)])
+def test_gemm_lds_free_triangular_complex(T, M, N, beta, split, pad, form, monkeypatch):
+    """Complex fp64 triangular products on the LDS-free kernel through the
+    real view (TRSM_LF_CPLX_TRI=0: the LDS tile): a ragged last row tile,
+    odd M (complex rows stay whole: a real row pair never straddles two
+    tiles), ragged N, a C term, rows routed to D2."""
+    monkeypatch.setenv("TRSM_LF_CPLX_TRI", form)
+    print(f"case c64 tri M={M} N={N} beta={beta} split={split} form={form}", flush=True)
+    gemm_case(T, "c64", M, N, M, beta, -0.75 + 0.25j, seed=M + N + split, a_lower=True, split=split,
+              ldpad=pad, ldpad_a=pad, ldpad_b=pad)
+
+
 LF_CPLX_CASES = [
     # (M, N, K, ldpad, split, beta, gamma) in complex elements: the real view
     # 2M x N gives 16 x 32 = 512 tiles of 128 x 128

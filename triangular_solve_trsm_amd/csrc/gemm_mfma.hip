@@ -1450,6 +1450,22 @@ hipError_t launch_lf_batched_cplx(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Complex fp64 triangular solve products on gemm_lf_kernel through the real
+// view: folded pairs of 64-row real tiles, 16 NBT columns per wave.
+template <int RING, int NBT>
+hipError_t launch_lf_tri_cplx(const GemmDesc &g, hipStream_t st) {
+    GemmParams<cplx> pc;
+    dim3 grid;
+    hipError_t e = tile_params<cplx, 128, 128>(g, pc, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    GemmParams<double> p = real_view(pc);
+    p.tilesM = (int)(((p.M + 63) / 64 + 1) / 2);
+    p.tilesN = (int)((p.N + 64 * NBT - 1) / (64 * NBT));
+    grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
+    hipLaunchKernelGGL((gemm_lf_kernel<RING, NBT, true, true>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
 // fp64 and complex fp64 products that split-K would cut, on gemm_ks_kernel:
 // 64 x 16 tiles, KW = the split-K factor (at most 8) waves on each.
 template <int KW>
@@ -1514,6 +1530,7 @@ bool use_ks(int dtype, const GemmDesc &g) {
 // 8192^2: 168 us with the 64 x 32 wave tile and a ring of 3, 162 with 4,
 // 158 with 5; a 64 x 64 wave tile (one wave per SIMD) 178 us; the LDS tile
 // (64 x 128) 171 us.
+template <int RING = 5>
 hipError_t launch_lf_tri(const GemmDesc &g, hipStream_t st) {
     GemmParams<double> p;
     dim3 grid;
@@ -1523,7 +1540,7 @@ hipError_t launch_lf_tri(const GemmDesc &g, hipStream_t st) {
     p.tilesM = (int)((T + 1) / 2);  // row-tile pairs
     p.tilesN = (int)((g.N + 127) / 128);
     grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
-    hipLaunchKernelGGL((gemm_lf_kernel<5, 2, true>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_lf_kernel<RING, 2, true>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1631,13 +1648,29 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
         const int64_t pairs = ((Mr + 63) / 64 + 1) / 2;
         if constexpr (std::is_same<T, double>::value) {
+            const bool lf = use_gemm_lf() && aligned16(g.A, g.lda, 8) && aligned16(g.Bm, g.ldb, 8);
             if (pairs * ((g.N + 127) / 128) >= 512) {
-                if (use_gemm_lf() && aligned16(g.A, g.lda, 8) && aligned16(g.Bm, g.ldb, 8))
-                    return launch_lf_tri(g, st);
+                if (lf) return launch_lf_tri(g, st);
                 return launch_tile<T, 64, 128, KT>(g, st);
             }
+            // 256 to 511 such workgroups (fp64 4096^2: 1024 x 4096 products,
+            // one workgroup per CU): a ring of three, as for complex fp64
+            // below; fp64 4096^2 1.372 -> 1.322 ms against the 64 x 32 LDS
+            // tile (whole solves, same box)
+            if (lf && pairs * ((g.N + 127) / 128) >= 256) return launch_lf_tri<3>(g, st);
         }
         if constexpr (std::is_same<T, cplx>::value) {
+            // the real view on the LDS-free kernel once the folded pairs give
+            // 256 workgroups of 128 columns (64 x 32 per wave, a ring of
+            // three chunks); TRSM_LF_CPLX_TRI=0 keeps the LDS tiles.
+            // Measured (whole solves, two rounds on one box, against the
+            // 64 x 64 LDS tile): complex 8192 x 2048 8.58-8.61 -> 8.48-8.50 ms,
+            // 4096^2 4.44-4.45 -> 4.34-4.35 ms; rings of five (64 x 32) and
+            // four (64 x 16 per wave, 512 workgroups) were within 1 % behind.
+            const char *et = std::getenv("TRSM_LF_CPLX_TRI");
+            if (use_gemm_lf() && !(et && et[0] == '0') && aligned16(g.A, g.lda, 16) &&
+                aligned16(g.Bm, g.ldb, 16) && pairs * ((g.N + 127) / 128) >= 256)
+                return launch_lf_tri_cplx<3, 2>(g, st);
             if (pairs * ((g.N + 63) / 64) >= 512) return launch_tile<T, 64, 64, KT>(g, st);
         }
     }
