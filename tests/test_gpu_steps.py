@@ -157,16 +157,19 @@ def test_gemm_lds_free_edges(T, dtype, case, lf, monkeypatch):
 
 @pytest.mark.parametrize("lf", ["1", "0"])
 @pytest.mark.parametrize("case", LF_CASES)
-def test_gemm_lds_free_f32_256_tiles(T, case, lf, monkeypatch):
-    """fp32 products with 256 to 511 workgroups of 128 x 128 (here 8 x 32 =
-    256) take the LDS-free kernel with a ring of three chunks (the ring of
-    five above 512): the same edge cases as above on half the rows."""
+@pytest.mark.parametrize("dtype", ["f32", "f64"])
+def test_gemm_lds_free_256_tiles(T, dtype, case, lf, monkeypatch):
+    """fp32 and fp64 products with 256 to 511 tiles of 128 x 128 (here 8 x 32
+    = 256) take the LDS-free kernels on half-width workgroups, two per CU,
+    with a ring of three chunks (fp32: the ring of five above 512): the
+    same edge cases as above on half the rows."""
     monkeypatch.setenv("TRSM_GEMM_LF", lf)
     M, N, K, ldpad, split, beta, gamma = case
     M = M // 2
-    pa = ldpad + (-(M + ldpad)) % 4
-    pb = ldpad + (-(K + ldpad)) % 4
-    gemm_case(T, "f32", M, N, K, beta, gamma, seed=K + M + 1, ldpad=ldpad, ldpad_a=pa, ldpad_b=pb,
+    per = 2 if dtype == "f64" else 4
+    pa = ldpad + (-(M + ldpad)) % per
+    pb = ldpad + (-(K + ldpad)) % per
+    gemm_case(T, dtype, M, N, K, beta, gamma, seed=K + M + 1, ldpad=ldpad, ldpad_a=pa, ldpad_b=pb,
               split=min(split, M))
 
 
@@ -223,6 +226,18 @@ LF_CPLX_CASES = [
     (1000, 4000, 501, 1, 37, 0.5 + 0.25j, -1.0),    # odd split
     (1000, 3999, 128, 0, 0, 1.0, -1.0 - 1j),        # ragged N
 ]
+
+
+@pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("case", LF_CPLX_CASES)
+def test_gemm_lds_free_complex_256_tiles(T, case, lf, monkeypatch):
+    """Complex fp64 products whose real view gives 256 to 511 tiles of
+    128 x 128 (here 8 x 32) on half-width LDS-free workgroups, two per CU:
+    the cases below on half the complex rows."""
+    monkeypatch.setenv("TRSM_GEMM_LF", lf)
+    M, N, K, ldpad, split, beta, gamma = case
+    M = M // 2
+    gemm_case(T, "c64", M, N, K, beta, gamma, seed=K + M + 2, ldpad=ldpad, split=min(split, M))
 
 
 @pytest.mark.parametrize("lf", ["1", "0"])

@@ -1373,6 +1373,32 @@ hipError_t launch_lf_batched(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// fp64 updates on 128 x 32 NBT workgroups of gemm_lf_kernel (64 x 16 NBT per
+// wave), sized for two workgroups per CU.
+template <int RING, int NBT>
+hipError_t launch_lf_n(const GemmDesc &g, hipStream_t st) {
+    GemmParams<double> p;
+    dim3 grid;
+    hipError_t e = tile_params<double, 128, 128>(g, p, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    p.tilesM = (int)((g.M + 127) / 128);
+    p.tilesN = (int)((g.N + 32 * NBT - 1) / (32 * NBT));
+    grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
+    hipLaunchKernelGGL((gemm_lf_kernel<RING, NBT, false>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+// Updates with 256 to 511 tiles of 128 x 128 in rounds of 256 more than 3/4
+// full, on 128 x 64 workgroups (64 x 32 per wave, two per CU, as fp32 does)
+// instead of the LDS tiles (TRSM_LF_MID=0 turns this off for tuning).
+// Measured (whole solves, three rounds on one box): fp64 4096^2 1.326 ->
+// 1.233 ms, 8192 x 2048 2.723 -> 2.709; complex 8192 x 2048 8.46-8.48 ->
+// 8.44, 8192 x 1024 5.040 -> 5.008, 2048^2 0.847 -> 0.832 ms.
+bool use_lf_mid(int64_t t128) {
+    const char *e = std::getenv("TRSM_LF_MID");
+    return !(e && e[0] == '0') && t128 >= 256 && t128 < 512 && 4 * t128 > 3 * 256 * ((t128 + 255) / 256);
+}
+
 // The real view of a complex fp64 product for the LDS-free kernels: M and
 // K doubled (real rows and k), Bm, C, D and D2 read as interleaved real with
 // doubled leading dimensions, A kept in complex addressing (lda in complex
@@ -1447,6 +1473,21 @@ hipError_t launch_lf_batched_cplx(const GemmDesc &g, hipStream_t st) {
         else
             hipLaunchKernelGGL((gemm_lf_kernel<RING, 1, false, true, true, false>), grid, dim3(256), 0, st, p);
     }
+    return hipGetLastError();
+}
+
+// Complex fp64 updates through the real view on 128 x 32 NBT workgroups.
+template <int RING, int NBT>
+hipError_t launch_lf_cplx_n(const GemmDesc &g, hipStream_t st) {
+    GemmParams<cplx> pc;
+    dim3 grid;
+    hipError_t e = tile_params<cplx, 128, 128>(g, pc, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    GemmParams<double> p = real_view(pc);
+    p.tilesM = (int)((p.M + 127) / 128);
+    p.tilesN = (int)((p.N + 32 * NBT - 1) / (32 * NBT));
+    grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
+    hipLaunchKernelGGL((gemm_lf_kernel<RING, NBT, false, true>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1687,6 +1728,9 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
                 4 * t128 >= 3 * 512 * ((t128 + 511) / 512) && aligned16(g.A, g.lda, 16) &&
                 aligned16(g.Bm, g.ldb, 16))
                 return launch_lf_cplx(g, st);
+            if (use_gemm_lf() && !(ec && ec[0] == '0') && Mr > 64 && use_lf_mid(t128) &&
+                aligned16(g.A, g.lda, 16) && aligned16(g.Bm, g.ldb, 16))
+                return launch_lf_cplx_n<3, 2>(g, st);
         }
         if constexpr (GemmTraits<T>::kCplx) {
             if (((Mr + 63) / 64) * ((g.N + 127) / 128) >= 2048) return launch_tile<T, 64, 128, KT>(g, st);
@@ -1704,6 +1748,11 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
                     if (use_gemm_lf()) return launch_lf(g, st);
                 }
                 return launch_tile<T, 128, 128, KT>(g, st);
+            }
+            if constexpr (std::is_same<T, double>::value) {
+                if (use_gemm_lf() && Mr > 64 && use_lf_mid(t128) && aligned16(g.A, g.lda, 8) &&
+                    aligned16(g.Bm, g.ldb, 8))
+                    return launch_lf_n<3, 2>(g, st);
             }
             if (((Mr + 127) / 128) * ((g.N + 63) / 64) >= 2048) return launch_tile<T, 128, 64, KT>(g, st);
         }
