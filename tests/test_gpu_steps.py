@@ -186,12 +186,14 @@ def test_gemm_lds_free_triangular_f32_256(T, M, N, lf, monkeypatch):
 
 @pytest.mark.parametrize("lf", ["1", "0"])
 @pytest.mark.parametrize("M,N,beta,split,pad", [(1024, 4096, 0.0, 0, 0), (1000, 4000, 0.0, 0, 1),
-                                                (960, 4096, 1.5, 0, 0), (1023, 3999, -0.5, 130, 2)])
+                                                (960, 4096, 1.5, 0, 0), (1023, 3999, -0.5, 130, 2),
+                                                (1024, 2048, 0.0, 0, 0), (1000, 2047, 1.0, 37, 1)])
 def test_gemm_lds_free_triangular_f64_256(T, M, N, beta, split, pad, lf, monkeypatch):
     """fp64 triangular products with 256 to 511 folded workgroups of 128
-    columns on the LDS-free ring of three (TRSM_GEMM_LF=0: the LDS tile):
-    ragged last row tile, odd tile count, odd M and N, a C term, rows
-    routed to D2 below a split inside a row pair."""
+    columns on the LDS-free ring of three, and with fewer (N = 2048) on 64
+    columns per workgroup (TRSM_GEMM_LF=0: the LDS tile): ragged last row
+    tile, odd tile count, odd M and N, a C term, rows routed to D2 below a
+    split inside a row pair."""
     monkeypatch.setenv("TRSM_GEMM_LF", lf)
     print(f"case f64 tri M={M} N={N} beta={beta} split={split} lf={lf}", flush=True)
     gemm_case(T, "f64", M, N, M, beta, -0.75, seed=M + N + split, a_lower=True, split=split,
@@ -200,10 +202,12 @@ def test_gemm_lds_free_triangular_f64_256(T, M, N, beta, split, pad, lf, monkeyp
 
 @pytest.mark.parametrize("form", ["1", "0"])
 @pytest.mark.parametrize("M,N,beta,split,pad", [(1024, 2048, 0.0, 0, 0), (1000, 2000, 0.0, 0, 1),
-                                                (999, 2048, 1.0 - 0.5j, 0, 0), (1024, 2047, 0.5, 130, 2)])
+                                                (999, 2048, 1.0 - 0.5j, 0, 0), (1024, 2047, 0.5, 130, 2),
+                                                (1024, 1024, 0.0, 0, 0), (999, 1023, 0.5j, 65, 1)])
 def test_gemm_lds_free_triangular_complex(T, M, N, beta, split, pad, form, monkeypatch):
     """Complex fp64 triangular products on the LDS-free kernel through the
-    real view (TRSM_LF_CPLX_TRI=0: the LDS tile): a ragged last row tile,
+    real view, 64 x 32 per wave and (N = 1024) 64 x 16 per wave
+    (TRSM_LF_CPLX_TRI=0: the LDS tile): a ragged last row tile,
     odd M (complex rows stay whole: a real row pair never straddles two
     tiles), ragged N, a C term, rows routed to D2."""
     monkeypatch.setenv("TRSM_LF_CPLX_TRI", form)

@@ -1571,7 +1571,7 @@ bool use_ks(int dtype, const GemmDesc &g) {
 // 8192^2: 168 us with the 64 x 32 wave tile and a ring of 3, 162 with 4,
 // 158 with 5; a 64 x 64 wave tile (one wave per SIMD) 178 us; the LDS tile
 // (64 x 128) 171 us.
-template <int RING = 5>
+template <int RING = 5, int NBT = 2>
 hipError_t launch_lf_tri(const GemmDesc &g, hipStream_t st) {
     GemmParams<double> p;
     dim3 grid;
@@ -1579,9 +1579,9 @@ hipError_t launch_lf_tri(const GemmDesc &g, hipStream_t st) {
     if (e != hipSuccess || grid.x == 0) return e;
     const int64_t T = (g.M + 63) / 64;
     p.tilesM = (int)((T + 1) / 2);  // row-tile pairs
-    p.tilesN = (int)((g.N + 127) / 128);
+    p.tilesN = (int)((g.N + 64 * NBT - 1) / (64 * NBT));
     grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
-    hipLaunchKernelGGL((gemm_lf_kernel<RING, 2, true>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_lf_kernel<RING, NBT, true>), grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1699,6 +1699,9 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
             // below; fp64 4096^2 1.372 -> 1.322 ms against the 64 x 32 LDS
             // tile (whole solves, same box)
             if (lf && pairs * ((g.N + 127) / 128) >= 256) return launch_lf_tri<3>(g, st);
+            // fewer: 64 columns per workgroup (64 x 16 per wave, a ring of four)
+            // while that gives 256 (fp64 4096 x 2048: 0.797 -> 0.767 ms)
+            if (lf && pairs * ((g.N + 63) / 64) >= 256) return launch_lf_tri<4, 1>(g, st);
         }
         if constexpr (std::is_same<T, cplx>::value) {
             // the real view on the LDS-free kernel once the folded pairs give
@@ -1712,6 +1715,11 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
             if (use_gemm_lf() && !(et && et[0] == '0') && aligned16(g.A, g.lda, 16) &&
                 aligned16(g.Bm, g.ldb, 16) && pairs * ((g.N + 127) / 128) >= 256)
                 return launch_lf_tri_cplx<3, 2>(g, st);
+            // (fewer: 64 x 16 per wave while that gives 256 workgroups;
+            // complex 8192 x 1024 5.019 -> 4.910 ms, 4096 x 2048 2.585 -> 2.544)
+            if (use_gemm_lf() && !(et && et[0] == '0') && aligned16(g.A, g.lda, 16) &&
+                aligned16(g.Bm, g.ldb, 16) && pairs * ((g.N + 63) / 64) >= 256)
+                return launch_lf_tri_cplx<4, 1>(g, st);
             if (pairs * ((g.N + 63) / 64) >= 512) return launch_tile<T, 64, 64, KT>(g, st);
         }
     }
