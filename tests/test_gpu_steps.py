@@ -233,6 +233,24 @@ LF_CPLX_CASES = [
 
 
 @pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("case", LF_CASES)
+@pytest.mark.parametrize("dtype", ["f64", "c64"])
+def test_gemm_lds_free_64_tiles(T, dtype, case, lf, monkeypatch):
+    """fp64 and complex fp64 products with 64 to 255 tiles of 128 x 128 (here
+    a quarter of the rows: 4 x 32 = 128 for fp64, the real view of complex
+    the same) on 128 x 32 LDS-free workgroups: the edge cases above."""
+    monkeypatch.setenv("TRSM_GEMM_LF", lf)
+    M, N, K, ldpad, split, beta, gamma = case
+    M = M // 4 if dtype == "f64" else M // 8
+    pa = ldpad + (-(M + ldpad)) % 2 if dtype == "f64" else ldpad
+    pb = ldpad + (-(K + ldpad)) % 2 if dtype == "f64" else ldpad
+    if dtype == "c64":
+        beta, gamma = beta * (1 - 0.5j), gamma * (0.5 + 1j)
+    gemm_case(T, dtype, M, N, K, beta, gamma, seed=K + M + 3, ldpad=ldpad, ldpad_a=pa, ldpad_b=pb,
+              split=min(split, M))
+
+
+@pytest.mark.parametrize("lf", ["1", "0"])
 @pytest.mark.parametrize("case", LF_CPLX_CASES)
 def test_gemm_lds_free_complex_256_tiles(T, case, lf, monkeypatch):
     """Complex fp64 products whose real view gives 256 to 511 tiles of

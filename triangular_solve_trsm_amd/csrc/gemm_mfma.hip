@@ -1476,6 +1476,18 @@ hipError_t launch_lf_batched_cplx(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Updates with 64 to 255 such tiles: 128 x 32 workgroups (64 x 16 per wave,
+// a ring of four), four times the workgroups.  TRSM_LF_LOW sets the lower
+// bound (0: off).  Measured (whole solves, three rounds on one box, against
+// the 64 x 32 and 64 x 64 LDS tiles): fp64 2048^2 0.301 -> 0.287 ms,
+// 8192 x 1024 1.565 -> 1.524; complex 2048^2 0.808 -> 0.790, 8192 x 512
+// 2.86 -> 2.82 ms.
+bool use_lf_low(int64_t t128) {
+    const char *e = std::getenv("TRSM_LF_LOW");
+    const int64_t lo = e ? std::atoll(e) : 64;
+    return lo > 0 && t128 >= lo && t128 < 256;
+}
+
 // Complex fp64 updates through the real view on 128 x 32 NBT workgroups.
 template <int RING, int NBT>
 hipError_t launch_lf_cplx_n(const GemmDesc &g, hipStream_t st) {
@@ -1739,6 +1751,9 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
             if (use_gemm_lf() && !(ec && ec[0] == '0') && Mr > 64 && use_lf_mid(t128) &&
                 aligned16(g.A, g.lda, 16) && aligned16(g.Bm, g.ldb, 16))
                 return launch_lf_cplx_n<3, 2>(g, st);
+            if (use_gemm_lf() && !(ec && ec[0] == '0') && Mr > 64 && use_lf_low(t128) &&
+                aligned16(g.A, g.lda, 16) && aligned16(g.Bm, g.ldb, 16))
+                return launch_lf_cplx_n<4, 1>(g, st);
         }
         if constexpr (GemmTraits<T>::kCplx) {
             if (((Mr + 63) / 64) * ((g.N + 127) / 128) >= 2048) return launch_tile<T, 64, 128, KT>(g, st);
@@ -1761,6 +1776,9 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
                 if (use_gemm_lf() && Mr > 64 && use_lf_mid(t128) && aligned16(g.A, g.lda, 8) &&
                     aligned16(g.Bm, g.ldb, 8))
                     return launch_lf_n<3, 2>(g, st);
+                if (use_gemm_lf() && Mr > 64 && use_lf_low(t128) && aligned16(g.A, g.lda, 8) &&
+                    aligned16(g.Bm, g.ldb, 8))
+                    return launch_lf_n<4, 1>(g, st);
             }
             if (((Mr + 127) / 128) * ((g.N + 63) / 64) >= 2048) return launch_tile<T, 128, 64, KT>(g, st);
         }
