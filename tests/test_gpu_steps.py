@@ -174,11 +174,12 @@ def test_gemm_lds_free_256_tiles(T, dtype, case, lf, monkeypatch):
 
 
 @pytest.mark.parametrize("lf", ["1", "0"])
-@pytest.mark.parametrize("M,N", [(1000, 4000), (960, 4096), (1023, 4000), (1024, 3970)])
+@pytest.mark.parametrize("M,N", [(1000, 4000), (960, 4096), (1023, 4000), (1024, 3970), (1024, 2048),
+                                 (999, 1100)])
 def test_gemm_lds_free_triangular_f32_256(T, M, N, lf, monkeypatch):
     """Triangular fp32 products with 256 folded workgroups (8 pairs of row
-    tiles x 32 column blocks) on the ring of three: ragged last row tile, an
-    odd tile count, odd M, ragged N."""
+    tiles x 32 column blocks) and with 64 to 255 (N = 2048, 1100) on the ring
+    of three: ragged last row tile, an odd tile count, odd M, ragged N."""
     monkeypatch.setenv("TRSM_GEMM_LF", lf)
     pa = (-M) % 4
     gemm_case(T, "f32", M, N, M, 0.0, -0.75, seed=M + N + 1, a_lower=True, ldpad_a=pa, ldpad_b=pa)
@@ -234,16 +235,17 @@ LF_CPLX_CASES = [
 
 @pytest.mark.parametrize("lf", ["1", "0"])
 @pytest.mark.parametrize("case", LF_CASES)
-@pytest.mark.parametrize("dtype", ["f64", "c64"])
+@pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])
 def test_gemm_lds_free_64_tiles(T, dtype, case, lf, monkeypatch):
-    """fp64 and complex fp64 products with 64 to 255 tiles of 128 x 128 (here
-    a quarter of the rows: 4 x 32 = 128 for fp64, the real view of complex
-    the same) on 128 x 32 LDS-free workgroups: the edge cases above."""
+    """fp32, fp64 and complex fp64 products with 64 to 255 tiles of 128 x 128
+    (here a quarter of the rows: 4 x 32 = 128; the real view of complex the
+    same) on 128 x 32 LDS-free workgroups: the edge cases above."""
     monkeypatch.setenv("TRSM_GEMM_LF", lf)
     M, N, K, ldpad, split, beta, gamma = case
-    M = M // 4 if dtype == "f64" else M // 8
-    pa = ldpad + (-(M + ldpad)) % 2 if dtype == "f64" else ldpad
-    pb = ldpad + (-(K + ldpad)) % 2 if dtype == "f64" else ldpad
+    M = M // 8 if dtype == "c64" else M // 4
+    per = {"f32": 4, "f64": 2, "c64": 1}[dtype]
+    pa = ldpad + (-(M + ldpad)) % per
+    pb = ldpad + (-(K + ldpad)) % per
     if dtype == "c64":
         beta, gamma = beta * (1 - 0.5j), gamma * (0.5 + 1j)
     gemm_case(T, dtype, M, N, K, beta, gamma, seed=K + M + 3, ldpad=ldpad, ldpad_a=pa, ldpad_b=pb,

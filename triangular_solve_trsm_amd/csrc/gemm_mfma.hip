@@ -1683,6 +1683,9 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
                 // workgroups, two per CU; 0.659 -> 0.652 ms on 4096^2)
                 if (lf && p128 >= 256 && 4 * p128 > 3 * 256 * ((p128 + 255) / 256))
                     return launch_lf32<3, 1, true, 2>(g, st);
+                // 64 to 255: the same form (fp32 2048^2: 0.174 -> 0.167 ms,
+                // 4096 x 2048: 0.443 -> 0.428 ms against the LDS tiles)
+                if (lf && p128 >= 64 && p128 < 256) return launch_lf32<3, 1, true, 2>(g, st);
                 // fewer workgroups: the LDS tile, 64 x 64 while that still
                 // gives 512 folded workgroups
                 if (pairs * ((g.N + 63) / 64) >= 512) return launch_tile<T, 64, 64, KT>(g, st);
@@ -1694,6 +1697,11 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
                 // two per CU: twice the workgroups; 0.649 -> 0.637 ms on 4096^2)
                 if (g.M > 64 && t128 >= 256 && t128 < 512 && 4 * t128 > 3 * 256 * ((t128 + 255) / 256))
                     return launch_lf32<3, 2, false, 2>(g, st);
+                // 64 to 255: 128 x 32 workgroups (64 x 16 per wave, a ring of
+                // four), four per tile (fp32 2048^2 0.174 -> 0.166 ms,
+                // 4096 x 1024 0.330 -> 0.319 ms; with the triangular rule
+                // above 2048^2 takes 0.159 ms)
+                if (g.M > 64 && t128 >= 64 && t128 < 256) return launch_lf32<4, 1, false, 2>(g, st);
             }
         }
     }
