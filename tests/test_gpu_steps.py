@@ -253,6 +253,36 @@ def test_gemm_lds_free_64_tiles(T, dtype, case, lf, monkeypatch):
 
 
 @pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("div", [1, 2, 8])
+@pytest.mark.parametrize("case", LF_CPLX_CASES)
+def test_gemm_lds_free_complex_f32(T, case, div, lf, monkeypatch):
+    """Complex fp32 products on the LDS-free fp32 kernel through the real
+    view (one 16-byte A load feeds two MFMA steps as (re, im) and (-im, re);
+    TRSM_LF_C32=0: the LDS tiles), at 512, 256 and 64 tiles of 128 x 128
+    (the cases below on all, half and an eighth of the rows): every K
+    modulo the chunk (8 complex k), K = 0, NaN past K in Bm, odd M, ragged
+    N, the D2 split, complex beta and gamma."""
+    monkeypatch.setenv("TRSM_LF_C32", lf)
+    M, N, K, ldpad, split, beta, gamma = case
+    M = M // div
+    print(f"case c32 M={M} N={N} K={K} split={split} lf={lf}", flush=True)
+    gemm_case(T, "c32", M, N, K, beta, gamma, seed=K + M + 5, ldpad=ldpad, split=min(split, M))
+
+
+@pytest.mark.parametrize("lf", ["1", "0"])
+@pytest.mark.parametrize("M,N,beta,split,pad", [(1000, 4000, 0.0, 0, 0), (1024, 2048, 0.5j, 0, 1),
+                                                (999, 1024, 0.0, 65, 0), (500, 4096, 1.0, 0, 2)])
+def test_gemm_lds_free_triangular_c32(T, M, N, beta, split, pad, lf, monkeypatch):
+    """Complex fp32 triangular products on the LDS-free fp32 forms through
+    the real view (folded pairs of 64 real rows; 512, 256 and 128 folded
+    workgroups of 128 columns), against the LDS tiles (TRSM_LF_C32=0)."""
+    monkeypatch.setenv("TRSM_LF_C32", lf)
+    print(f"case c32 tri M={M} N={N} beta={beta} split={split} lf={lf}", flush=True)
+    gemm_case(T, "c32", M, N, M, beta, -0.75 + 0.25j, seed=M + N + split, a_lower=True, split=split,
+              ldpad=pad, ldpad_a=pad, ldpad_b=pad)
+
+
+@pytest.mark.parametrize("lf", ["1", "0"])
 @pytest.mark.parametrize("case", LF_CPLX_CASES)
 def test_gemm_lds_free_complex_256_tiles(T, case, lf, monkeypatch):
     """Complex fp64 products whose real view gives 256 to 511 tiles of

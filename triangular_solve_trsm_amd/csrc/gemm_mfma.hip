@@ -1044,7 +1044,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_ks_kernel(GemmParams<double> p) 
 //     Bm loads there.
 // NBT and TRI as for gemm_lf_kernel; MINB: workgroups per CU the register
 // budget is sized for.
-template <int RING, int NBT, bool TRI, int MINB = 1>
+// CPLX: complex fp32 through the real 2 x 2 embedding, p describing the real
+// view as for gemm_lf_kernel (M, K, split in real rows and k; Bm, C, D, D2
+// interleaved storage read as real with doubled leading dimensions; A in
+// complex addressing, lda in complex elements, extA in floats).  Real rows
+// 4c .. 4c+3 are complex rows 2c, 2c+1, so one 16-byte load of A(2c, k) and
+// A(2c+1, k) at complex k = 2q + h feeds MFMA steps s = 2h (re, im, re, im)
+// and s = 2h+1 (-im, re, -im, re): two A loads per chunk instead of four.
+// The four items of a lane's output quadruple are two complex elements, so
+// C is scaled by sc and the result by gamma as complex numbers.
+template <int RING, int NBT, bool TRI, int MINB = 1, bool CPLX = false>
 __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1058,11 +1067,15 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
     const int64_t lda = p.lda, ldb = p.ldb;
     uint32_t offA[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) offA[s] = (uint32_t)((4 * c16 + (4 * q + s) * lda) * 4);
+    for (int s = 0; s < 4; ++s) {
+        if constexpr (CPLX) offA[s] = (uint32_t)((2 * c16 + (2 * q + (s & 1)) * lda) * 8);  // s < 2 used
+        else offA[s] = (uint32_t)((4 * c16 + (4 * q + s) * lda) * 4);
+    }
     uint32_t offB[NBT];
 #pragma unroll
     for (int b = 0; b < NBT; ++b) offB[b] = (uint32_t)((4 * q + (c16 + 16 * (int64_t)b) * ldb) * 4);
     const float sc = (float)p.sc.re, gamma = (float)p.gamma.re;
+    const float sci = (float)p.sc.im, gammai = (float)p.gamma.im;  // complex only
 
     auto run_tile = [&](const int64_t r0, const int64_t c0, const int64_t K) {
         f4 acc[4][NBT];
@@ -1084,8 +1097,16 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
                             if (r + a < p.M) x[a] = col[r + a];
                     }
                 }
+                if constexpr (CPLX) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) acc[a][b][v] = sc * x[a];
+                    for (int h = 0; h < 2; ++h) {  // complex sc * C
+                        acc[2 * h][b][v] = sc * x[2 * h] - sci * x[2 * h + 1];
+                        acc[2 * h + 1][b][v] = sc * x[2 * h + 1] + sci * x[2 * h];
+                    }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) acc[a][b][v] = sc * x[a];
+                }
             }
         }
 
@@ -1093,8 +1114,13 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
         auto load = [&](int slot, int64_t k0, bool live) {
             const int64_t oa = r0 + k0 * lda;
             const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, live ? (p.extA - oa) * 4 : 0);
+            if constexpr (CPLX) {
+                ra[slot][0] = __builtin_bit_cast(f4, ld16<true>(rsa, offA[0]));
+                ra[slot][1] = __builtin_bit_cast(f4, ld16<true>(rsa, offA[1]));
+            } else {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) ra[slot][s] = __builtin_bit_cast(f4, ld16<true>(rsa, offA[s]));
+                for (int s = 0; s < 4; ++s) ra[slot][s] = __builtin_bit_cast(f4, ld16<true>(rsa, offA[s]));
+            }
             const int64_t ob = k0 + c0 * ldb;
             const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, live ? (p.extB - ob) * 4 : 0);
 #pragma unroll
@@ -1102,12 +1128,21 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
         };
         auto compute = [&](const f4 (&a4)[4], const f4 (&bq)[NBT]) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < 4; ++s) {
+                f4 av;
+                if constexpr (CPLX) {
+                    const f4 x = a4[s >> 1];
+                    if (s & 1) av = f4{-x[1], x[0], -x[3], x[2]};
+                    else av = x;
+                } else {
+                    av = a4[s];
+                }
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
 #pragma unroll
                     for (int b = 0; b < NBT; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[s][a], bq[b][s], acc[a][b], 0, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bq[b][s], acc[a][b], 0, 0, 0);
+            }
         };
         const int64_t nkf = K / 16;  // full chunks
 #pragma unroll
@@ -1131,9 +1166,15 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
             const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, (p.extA - oa) * 4);
             const uint32_t dead = 0xfffffff0u;
             f4 ta[4], tb[NBT];
+            if constexpr (CPLX) {
+                // the real K is even: a complex k is whole or absent
+                ta[0] = __builtin_bit_cast(f4, ld16<true>(rsa, 4 * q < kr ? offA[0] : dead));
+                ta[1] = __builtin_bit_cast(f4, ld16<true>(rsa, 4 * q + 2 < kr ? offA[1] : dead));
+            } else {
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                ta[s] = __builtin_bit_cast(f4, ld16<true>(rsa, 4 * q + s < kr ? offA[s] : dead));
+                for (int s = 0; s < 4; ++s)
+                    ta[s] = __builtin_bit_cast(f4, ld16<true>(rsa, 4 * q + s < kr ? offA[s] : dead));
+            }
             const int64_t ob = k0 + c0 * ldb;
             const __amdgpu_buffer_rsrc_t rsb = make_rsrc(pB + ob, (p.extB - ob) * 4);
 #pragma unroll
@@ -1154,8 +1195,16 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
                 const int64_t r = r0 + 16 * q + 4 * v;
                 if (r >= p.M) continue;
                 float out[4];
+                if constexpr (CPLX) {
 #pragma unroll
-                for (int a = 0; a < 4; ++a) out[a] = gamma * acc[a][b][v];
+                    for (int h = 0; h < 2; ++h) {  // complex gamma * acc
+                        out[2 * h] = gamma * acc[2 * h][b][v] - gammai * acc[2 * h + 1][b][v];
+                        out[2 * h + 1] = gamma * acc[2 * h + 1][b][v] + gammai * acc[2 * h][b][v];
+                    }
+                } else {
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) out[a] = gamma * acc[a][b][v];
+                }
                 if (r + 3 < p.M && r + 3 < p.split) {
                     float *dst = p.D2 + j * p.ldd2 + r;
                     if (p.d2_vec) *reinterpret_cast<f4 *>(dst) = f4{out[0], out[1], out[2], out[3]};
@@ -1617,6 +1666,82 @@ hipError_t launch_lf32(const GemmDesc &g, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Complex fp32 products on gemm_lf32_kernel through the real view (as
+// real_view for complex fp64: M, K and split doubled, Bm, C, D, D2 read as
+// interleaved floats with doubled leading dimensions, A in complex
+// addressing with extA in floats).
+template <int RING, int NBT, bool TRI, int MINB = 1>
+hipError_t launch_lf32_cplx(const GemmDesc &g, hipStream_t st) {
+    GemmParams<cplx32> pc;
+    dim3 grid;
+    hipError_t e = tile_params<cplx32, 128, 128>(g, pc, grid);
+    if (e != hipSuccess || grid.x == 0) return e;
+    if (grid.y > 1) return hipErrorInvalidValue;
+    GemmParams<float> p{};
+    p.M = 2 * pc.M;
+    p.N = pc.N;
+    p.K = 2 * pc.K;
+    p.A = reinterpret_cast<const float *>(pc.A);
+    p.lda = pc.lda;
+    p.extA = 2 * pc.extA;
+    p.Bm = reinterpret_cast<const float *>(pc.Bm);
+    p.ldb = 2 * pc.ldb;
+    p.extB = 2 * pc.extB;
+    p.C = reinterpret_cast<const float *>(pc.C);
+    p.ldc = 2 * pc.ldc;
+    p.D = reinterpret_cast<float *>(pc.D);
+    p.ldd = 2 * pc.ldd;
+    p.D2 = reinterpret_cast<float *>(pc.D2);
+    p.ldd2 = 2 * pc.ldd2;
+    p.split = 2 * pc.split;
+    p.sc = pc.sc;
+    p.gamma = pc.gamma;
+    p.has_c = pc.has_c;
+    p.a_vec = pc.a_vec;
+    p.b_vec = pc.b_vec;
+    p.c_vec = pc.c_vec;
+    p.d_vec = pc.d_vec;
+    p.d2_vec = pc.d2_vec;
+    p.binner = 1;
+    if (TRI) {
+        p.tilesM = (int)(((p.M + 63) / 64 + 1) / 2);
+        p.tilesN = (int)((p.N + 64 * NBT - 1) / (64 * NBT));
+    } else {
+        p.tilesM = (int)((p.M + 127) / 128);
+        p.tilesN = (int)((p.N + 32 * NBT - 1) / (32 * NBT));
+    }
+    grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
+    hipLaunchKernelGGL((gemm_lf32_kernel<RING, NBT, TRI, MINB, true>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+// The LDS-free fp32 forms for complex fp32, by the fp32 rules on the real
+// view; TRSM_LF_C32=0 keeps the LDS tiles.
+hipError_t launch_c32_lf(const GemmDesc &g, hipStream_t st, bool &taken) {
+    taken = false;
+    const char *e = std::getenv("TRSM_LF_C32");
+    if ((e && e[0] == '0') || !use_gemm_lf() || g.batch > 1 || g.b_lower || !aligned16(g.A, g.lda, 8) ||
+        !aligned16(g.Bm, g.ldb, 8))
+        return hipSuccess;
+    const int64_t Mr = 2 * g.M;
+    const int64_t tN128 = (g.N + 127) / 128;
+    taken = true;
+    if (g.a_lower) {
+        const int64_t p128 = ((Mr + 63) / 64 + 1) / 2 * tN128;
+        if (p128 >= 512) return launch_lf32_cplx<5, 2, true>(g, st);
+        if (p128 >= 256 && 4 * p128 > 3 * 256 * ((p128 + 255) / 256)) return launch_lf32_cplx<3, 1, true, 2>(g, st);
+        if (p128 >= 64 && p128 < 256) return launch_lf32_cplx<3, 1, true, 2>(g, st);
+    } else if (Mr > 64) {
+        const int64_t t128 = ((Mr + 127) / 128) * tN128;
+        if (t128 >= 512 && 4 * t128 >= 3 * 512 * ((t128 + 511) / 512)) return launch_lf32_cplx<5, 4, false>(g, st);
+        if (t128 >= 256 && t128 < 512 && 4 * t128 > 3 * 256 * ((t128 + 255) / 256))
+            return launch_lf32_cplx<3, 2, false, 2>(g, st);
+        if (t128 >= 64 && t128 < 256) return launch_lf32_cplx<4, 1, false, 2>(g, st);
+    }
+    taken = false;
+    return hipSuccess;
+}
+
 // Macro tile, from timings on MI355X of the update and solve sequences of
 // blocked solves (fp32 4096^2, fp64 1024^2 .. 8192^2, complex 8192 x 2048):
 //   * 64 x 32 for the triangular solve products (each workgroup folds two
@@ -1704,6 +1829,11 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
                 if (g.M > 64 && t128 >= 64 && t128 < 256) return launch_lf32<4, 1, false, 2>(g, st);
             }
         }
+    }
+    if constexpr (std::is_same<T, cplx32>::value) {
+        bool taken = false;
+        const hipError_t e = launch_c32_lf(g, st, taken);
+        if (taken || e != hipSuccess) return e;
     }
     if (g.a_lower && !g.b_lower && g.batch <= 1) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
