@@ -13,7 +13,24 @@
 // that the next solve reads, so no copy is needed), and a lower-triangular A
 // skips the K-tiles right of each row tile's diagonal (the solve GEMM).
 //
-// gfx950 mapping:
+// Kernel families (launch_sized picks one by data type, shape and tile
+// count; the rules and the measurements behind them are next to it):
+//   * gemm_lf_kernel (fp64, complex fp64 through its real view) and
+//     gemm_lf32_kernel (fp32, complex fp32): no LDS; each wave streams its own
+//     A and Bm fragments into a ring of registers a few chunks of K ahead of
+//     the MFMAs.  They take the single products whose tiles give the chip
+//     enough waves (updates with 64 or more tiles of 128 x 128, triangular
+//     solve products with 64 or more folded pairs), and the inversion's
+//     larger batched doubling products;
+//   * gemm_kernel: LDS-staged macro tiles (below), for the remaining shapes:
+//     small and narrow products, unaligned operands, the inversion's small
+//     batched products, split-K chunks;
+//   * gemm_ks_kernel: fp64 and complex fp64 products with a long K and few
+//     output tiles, K split over the waves of one workgroup;
+//   * a product that splits K across workgroups (gemm_splitk_launch) runs
+//     its chunks as one batched launch and adds them in a fixed order.
+//
+// gemm_kernel's gfx950 mapping:
 //   * 256 threads = 2 x 2 wavefronts on a macro tile of MT x NT real rows x
 //     columns (32 x 32 up to 128 x 128 by launch shape, see launch_sized);
 //     each wave owns (MT/2) x (NT/2) as 16 x 16 tiles
@@ -1742,8 +1759,10 @@ hipError_t launch_c32_lf(const GemmDesc &g, hipStream_t st, bool &taken) {
     return hipSuccess;
 }
 
-// Macro tile, from timings on MI355X of the update and solve sequences of
-// blocked solves (fp32 4096^2, fp64 1024^2 .. 8192^2, complex 8192 x 2048):
+// Kernel and tile, from timings on MI355X of whole blocked solves.  Aligned
+// single products with enough tiles go to the LDS-free kernels first (the
+// rules in the branches below, with their measurements); what remains takes
+// an LDS tile of gemm_kernel:
 //   * 64 x 32 for the triangular solve products (each workgroup folds two
 //     row tiles, so twice as many column tiles keep the CUs busy; wider
 //     tiles for large fp64 and complex ones, see below), for
@@ -1760,7 +1779,8 @@ hipError_t launch_c32_lf(const GemmDesc &g, hipStream_t st, bool &taken) {
 //     results, which halves the operand traffic per product against 64 x 64
 //     tiles.  Measured on the left-looking updates of fp64 8192^2 (M = 1024,
 //     N = 8192): 61.3 -> 63.4 TFLOP/s at K = 7168, the solve 9.50 -> 9.27 ms.
-//     For fp32 and complex data it lost or spills.
+//     For fp32 and complex data it lost or spills.  (Aligned fp64 products
+//     of that size now run the LDS-free 128 x 128 form instead.)
 template <typename T, int KT>
 hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
     // The batched triangular products of the diagonal inversion (split-K
