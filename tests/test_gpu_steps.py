@@ -233,6 +233,23 @@ LF_CPLX_CASES = [
 ]
 
 
+@pytest.mark.parametrize("K,beta,split,pad", [(0, 1.5, 0, 0), (1, 1.0, 0, 1), (15, 0.0, 0, 2), (16, 1.0, 0, 0),
+                                          (17, -0.5, 100, 1), (100, 1.0, 37, 3), (2048, 1.0, 0, 0),
+                                          (2063, 0.5, 64, 1), (3000, 0.0, 0, 2)])
+def test_gemm_lds_free_f32_k_split(T, K, beta, split, pad, monkeypatch):
+    """fp32 products with 256 to 511 tiles of 128 x 128 and a long K run on
+    eight-wave workgroups whose two halves of K meet through LDS (forced
+    here from K = 1 with TRSM_LF32_KS=1): an empty first half (K < 32), K a
+    multiple of the chunk, ragged K (the second half takes the ragged
+    chunk), a C term, the D2 split, NaN past K in Bm."""
+    monkeypatch.setenv("TRSM_LF32_KS", "1")
+    M, N = 1000, 4000
+    pa = pad + (-(M + pad)) % 4
+    pb = pad + (-(K + pad)) % 4
+    print(f"case f32 k-split M={M} N={N} K={K} split={split}", flush=True)
+    gemm_case(T, "f32", M, N, K, beta, -1.0, seed=K + 7, ldpad=pad, ldpad_a=pa, ldpad_b=pb, split=split)
+
+
 @pytest.mark.parametrize("lf", ["1", "0"])
 @pytest.mark.parametrize("case", LF_CASES)
 @pytest.mark.parametrize("dtype", ["f32", "f64", "c64"])

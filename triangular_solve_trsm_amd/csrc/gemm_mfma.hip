@@ -1070,11 +1070,16 @@ __global__ __launch_bounds__(64 * KW) void gemm_ks_kernel(GemmParams<double> p) 
 // and s = 2h+1 (-im, re, -im, re): two A loads per chunk instead of four.
 // The four items of a lane's output quadruple are two complex elements, so
 // C is scaled by sc and the result by gamma as complex numbers.
-template <int RING, int NBT, bool TRI, int MINB = 1, bool CPLX = false>
-__global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> p) {
+template <int RING, int NBT, bool TRI, int MINB = 1, bool CPLX = false, int KS = 1>
+__global__ __launch_bounds__(256 * KS, MINB) void gemm_lf32_kernel(GemmParams<float> p) {
+    static_assert(KS == 1 || (KS == 2 && !TRI), "K split: rectangular products");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // KS = 2: eight waves, wave w on output quadrant w % 4 over half w / 4
+    // of K (the halves meet through LDS, second half into the first)
+    const int half = KS == 2 ? wave >> 2 : 0;
+    const int qw = KS == 2 ? wave & 3 : wave;
     const int c16 = lane & 15;
     const int q = lane >> 4;
     int tm, tn;
@@ -1094,7 +1099,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
     const float sc = (float)p.sc.re, gamma = (float)p.gamma.re;
     const float sci = (float)p.sc.im, gammai = (float)p.gamma.im;  // complex only
 
-    auto run_tile = [&](const int64_t r0, const int64_t c0, const int64_t K) {
+    auto run_tile = [&](const int64_t r0, const int64_t c0, const int64_t kb, const int64_t K) {
         f4 acc[4][NBT];
 #pragma unroll
         for (int b = 0; b < NBT; ++b) {
@@ -1103,7 +1108,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
             for (int v = 0; v < 4; ++v) {
                 const int64_t r = r0 + 16 * q + 4 * v;
                 float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if (p.has_c && j < p.N) {
+                if (p.has_c && j < p.N && half == 0) {
                     const float *col = p.C + j * p.ldc;
                     if (p.c_vec && r + 3 < p.M) {
                         const f4 c4 = *reinterpret_cast<const f4 *>(col + r);
@@ -1161,10 +1166,10 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
                         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[a], bq[b][s], acc[a][b], 0, 0, 0);
             }
         };
-        const int64_t nkf = K / 16;  // full chunks
+        const int64_t nkf = (K - kb) / 16;  // full chunks
 #pragma unroll
         for (int u = 0; u < RING; ++u) {
-            load(u, 16 * u, u < nkf);
+            load(u, kb + 16 * u, u < nkf);
             if constexpr (CPLX) __builtin_amdgcn_sched_barrier(0);
         }
         // whole rounds, then the last chunks (as gemm_lf_kernel)
@@ -1173,7 +1178,7 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
 #pragma unroll
             for (int u = 0; u < RING; ++u) {
                 compute(ra[u], rb[u]);
-                load(u, 16 * (kc + u + RING), kc + u + RING < nkf);
+                load(u, kb + 16 * (kc + u + RING), kc + u + RING < nkf);
                 // complex: keep each slot's loads with their slot, which holds
                 // every wait of the ring at its full depth (complex fp32
                 // 8192^2 16.5 -> 16.1 ms); for real data the free schedule
@@ -1184,9 +1189,9 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
 #pragma unroll
         for (int u = 0; u < RING; ++u)
             if (kc + u < nkf) compute(ra[u], rb[u]);  // uniform
-        const int kr = (int)(K - 16 * nkf);
+        const int kr = (int)(K - kb - 16 * nkf);
         if (kr > 0) {
-            const int64_t k0 = 16 * nkf;
+            const int64_t k0 = kb + 16 * nkf;
             const int64_t oa = r0 + k0 * lda;
             const __amdgpu_buffer_rsrc_t rsa = make_rsrc(pA + oa, (p.extA - oa) * 4);
             const uint32_t dead = 0xfffffff0u;
@@ -1209,6 +1214,23 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
                     tb[b][s] = __builtin_bit_cast(
                         float, __builtin_amdgcn_raw_buffer_load_b32(rsb, 4 * q + s < kr ? offB[b] + 4 * s : dead, 0, 0));
             compute(ta, tb);
+        }
+
+        if constexpr (KS == 2) {
+            // the second half's sums join the first's through LDS
+            __shared__ f4 red[4][4][NBT][64];
+            if (half == 1) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int b = 0; b < NBT; ++b) red[qw][a][b][lane] = acc[a][b];
+            }
+            __syncthreads();
+            if (half == 1) return;
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < NBT; ++b) acc[a][b] += red[qw][a][b][lane];
         }
 
 #pragma unroll
@@ -1257,12 +1279,18 @@ __global__ __launch_bounds__(256, MINB) void gemm_lf32_kernel(GemmParams<float> 
         const int t1 = T - 1 - tm;
         for (int pass = 0; pass < (t1 != tm ? 2 : 1); ++pass) {
             const int64_t r0 = (int64_t)(pass == 0 ? tm : t1) * 64;
-            run_tile(r0, c0, r0 + 64 < p.K ? r0 + 64 : p.K);
+            run_tile(r0, c0, 0, r0 + 64 < p.K ? r0 + 64 : p.K);
         }
     } else {
-        const int64_t r0 = (int64_t)tm * 128 + (wave & 1) * 64;
-        const int64_t c0 = (int64_t)tn * 32 * NBT + (int64_t)(wave >> 1) * 16 * NBT;
-        run_tile(r0, c0, p.K);
+        const int64_t r0 = (int64_t)tm * 128 + (qw & 1) * 64;
+        const int64_t c0 = (int64_t)tn * 32 * NBT + (int64_t)(qw >> 1) * 16 * NBT;
+        if constexpr (KS == 2) {
+            // halves split at a chunk boundary; the second takes the ragged end
+            const int64_t kmid = 16 * (((p.K + 15) / 16) / 2);
+            run_tile(r0, c0, half ? kmid : 0, half ? p.K : kmid);
+        } else {
+            run_tile(r0, c0, 0, p.K);
+        }
     }
 }
 
@@ -1673,7 +1701,7 @@ hipError_t launch_lf_tri(const GemmDesc &g, hipStream_t st) {
 
 // fp32 single products on gemm_lf32_kernel: the update tile 128 x 128
 // (64 x 64 per wave), the triangular product's wave tile 64 x 32.
-template <int RING, int NBT, bool TRI, int MINB = 1>
+template <int RING, int NBT, bool TRI, int MINB = 1, int KS = 1>
 hipError_t launch_lf32(const GemmDesc &g, hipStream_t st) {
     GemmParams<float> p;
     dim3 grid;
@@ -1687,7 +1715,7 @@ hipError_t launch_lf32(const GemmDesc &g, hipStream_t st) {
         p.tilesN = (int)((g.N + 32 * NBT - 1) / (32 * NBT));
     }
     grid = dim3((unsigned)(p.tilesM * p.tilesN), 1u);
-    hipLaunchKernelGGL((gemm_lf32_kernel<RING, NBT, TRI, MINB>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((gemm_lf32_kernel<RING, NBT, TRI, MINB, false, KS>), grid, dim3(256 * KS), 0, st, p);
     return hipGetLastError();
 }
 
@@ -1848,8 +1876,19 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
                     return launch_lf32<5, 4, false>(g, st);
                 // (the update there on 128 x 64 workgroups, 64 x 32 per wave,
                 // two per CU: twice the workgroups; 0.649 -> 0.637 ms on 4096^2)
-                if (g.M > 64 && t128 >= 256 && t128 < 512 && 4 * t128 > 3 * 256 * ((t128 + 255) / 256))
+                if (g.M > 64 && t128 >= 256 && t128 < 512 && 4 * t128 > 3 * 256 * ((t128 + 255) / 256)) {
+                    // K of 2048 and more: 64 x 64 per wave with K split over two
+                    // waves per SIMD (eight-wave workgroups, the halves added
+                    // through LDS) keeps two waves per SIMD on the larger wave
+                    // tile: fp32 8192^2 4.27 -> 4.18 ms, 8192 x 4096 2.195 ->
+                    // 2.162 ms, 4096^2 0.638 -> 0.634 ms; shorter K lost (the
+                    // 1024 x 4096 x 1024 update 82 -> 89 us).  TRSM_LF32_KS sets
+                    // the K bound (0: off)
+                    const char *ek = std::getenv("TRSM_LF32_KS");
+                    const int64_t kmin = ek ? std::atoll(ek) : 2048;
+                    if (kmin > 0 && g.K >= kmin) return launch_lf32<2, 4, false, 1, 2>(g, st);
                     return launch_lf32<3, 2, false, 2>(g, st);
+                }
                 // 64 to 255: 128 x 32 workgroups (64 x 16 per wave, a ring of
                 // four), four per tile (fp32 2048^2 0.174 -> 0.166 ms,
                 // 4096 x 1024 0.330 -> 0.319 ms; with the triangular rule
