@@ -118,6 +118,42 @@ def test_large_workloads_vs_oracle_and_residual(T, name):
     assert res <= 10 * cfg.m * u, res
 
 
+MID_SHAPES = [("f64", 4096, 4096), ("f64", 2048, 2048), ("f64", 4096, 2048), ("f64", 8192, 1024),
+              ("c64", 2048, 2048), ("c64", 4096, 2048), ("c64", 8192, 1024),
+              ("f32", 8192, 8192), ("f32", 4096, 2048), ("f32", 2048, 2048),
+              ("c32", 4096, 4096), ("c32", 8192, 2048), ("c32", 2048, 2048)]
+
+
+@pytest.mark.parametrize("schedule", ["left", "right"])
+@pytest.mark.parametrize("dtype,m,n", MID_SHAPES)
+def test_mid_size_solves_vs_oracle(T, dtype, m, n, schedule, monkeypatch):
+    """Whole solves at the table's block size whose products take the
+    LDS-free forms for 64 to 511 tiles (half- and quarter-width workgroups,
+    the K-split fp32 update, the complex fp32 mode, the complex triangular
+    forms and the inversion's larger batched products), in both phase-2
+    orders: one column of every 64-column tile plus the last against the
+    oracle, and the whole output through the residual bound."""
+    import torch
+    monkeypatch.setenv("TRSM_SCHEDULE", schedule)
+    print(f"case {dtype} m={m} n={n} {schedule}", flush=True)
+    L, B = make_problem(dtype, m, n, seed=m + n + (schedule == "left"))
+    a = 0.5 + 0.25j if dtype in CPLX else 0.5
+    Ad, Bd = to_dev(L), to_dev(B)
+    B0 = Bd.clone()
+    T.trsm_lln(Ad, Bd, a)
+    sync()
+    cols = tile_columns(n)
+    Xs = from_dev(Bd[:, torch.as_tensor(cols, device=Bd.device)])
+    check(dtype, Xs, oracle.solve(L, np.asfortranarray(B[:, cols]), a), f"{dtype} {m}x{n} {schedule}")
+    wide = torch.complex128 if dtype in CPLX else torch.float64
+    Lw = torch.tril(Ad.to(wide))
+    Xw, Bw = Bd.to(wide), B0.to(wide)
+    res = (torch.linalg.norm(Lw @ Xw - a * Bw) / (torch.linalg.norm(Lw) * torch.linalg.norm(Xw)
+                                                 + abs(a) * torch.linalg.norm(Bw))).item()
+    u = 2.0 ** -24 if dtype in ("f32", "c32") else 2.0 ** -53
+    assert res <= 10 * m * u, res
+
+
 # ---- regime edges, ragged blocks, layouts ----------------------------------
 
 EDGE_M = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129]
