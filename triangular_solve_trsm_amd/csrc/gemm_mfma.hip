@@ -1835,15 +1835,10 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
             if (use_inv_lf(g, 8)) return launch_lf_batched<4>(g, st);
         }
     }
-    // Triangular solve products (folded pairs of row tiles) with enough work
-    // for 512 workgroups on a wider tile: 64 x 128 for fp64, 64 x 64 for
-    // complex fp64.  Measured: fp64 8192^2 9.259 -> 9.218 ms, complex
-    // 8192 x 2048 9.574 -> 9.457 ms, complex 4096^2 4.904 -> 4.847 ms; with
-    // fewer workgroups (fp64 4096^2: 256) the wider tile lost (1.396 -> 1.428).
-    // fp32 single products whose 128-wide tiles fill the chip run without
-    // LDS (measured on fp32 8192^2: the solve 4.56 -> 4.30 ms, updates 6 %
-    // and triangular products 7 % faster; at fp32 4096^2, which gives half
-    // as many tiles, the LDS tiles stay ahead and are kept)
+    // fp32 single products with 64 or more 128-wide tiles run without LDS
+    // (first measured on fp32 8192^2: the solve 4.56 -> 4.30 ms, updates 6 %
+    // and triangular products 7 % faster than the LDS tiles; the smaller
+    // shapes followed once each had a form sized for them, below)
     if constexpr (std::is_same<T, float>::value) {
         if (g.batch <= 1 && !g.b_lower) {
             const bool lf = use_gemm_lf() && aligned16(g.A, g.lda, 4) && aligned16(g.Bm, g.ldb, 4);
@@ -1902,6 +1897,11 @@ hipError_t launch_sized(const GemmDesc &g, hipStream_t st) {
         const hipError_t e = launch_c32_lf(g, st, taken);
         if (taken || e != hipSuccess) return e;
     }
+    // Triangular solve products (folded pairs of row tiles) of fp64 and
+    // complex fp64: the LDS-free forms below; without them, wider LDS tiles
+    // once they give 512 folded workgroups, 64 x 128 for fp64 and 64 x 64 for
+    // complex (measured on those tiles: fp64 8192^2 9.259 -> 9.218 ms, complex
+    // 8192 x 2048 9.574 -> 9.457 ms), else 64 x 32.
     if (g.a_lower && !g.b_lower && g.batch <= 1) {
         const int64_t Mr = GemmTraits<T>::kCplx ? 2 * g.M : g.M;
         const int64_t pairs = ((Mr + 63) / 64 + 1) / 2;
