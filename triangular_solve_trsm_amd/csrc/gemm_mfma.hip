@@ -871,9 +871,21 @@ __global__ __launch_bounds__(256, 2) void gemm_lf_kernel(GemmParams<double> p) {
         const int64_t r0 = (int64_t)tm * 128 + (wave & 1) * 64;
         const int64_t c0 = (int64_t)tn * 32 * NBT + (int64_t)(wave >> 1) * 16 * NBT;
         // lower-triangular Bm: its rows above c0 are zero in these columns
-        // (complex: real k 2j starts complex column j)
-        const int64_t kb = (CPLX ? 2 : 1) * c0;
-        run_tile(r0, c0, BLO ? (kb < p.K ? kb : p.K) : 0, p.K);
+        if constexpr (BLO) {
+            // the K range of column block t shrinks with t: each workgroup
+            // takes blocks t and TN-1-t, one after the other, so every
+            // workgroup gets the same length of K (complex: real k 2j starts
+            // complex column j)
+            const int TN = (int)((p.N + 32 * NBT - 1) / (32 * NBT));
+            const int tn1 = TN - 1 - tn;
+            for (int pass = 0; pass < (tn1 != tn ? 2 : 1); ++pass) {
+                const int64_t cp = (int64_t)(pass == 0 ? tn : tn1) * 32 * NBT + (int64_t)(wave >> 1) * 16 * NBT;
+                const int64_t kb = (CPLX ? 2 : 1) * cp;
+                run_tile(r0, cp, kb < p.K ? kb : p.K, p.K);
+            }
+        } else {
+            run_tile(r0, c0, 0, p.K);
+        }
     }
 }
 
@@ -1466,6 +1478,7 @@ hipError_t launch_lf_batched(const GemmDesc &g, hipStream_t st) {
     } else {
         p.tilesM = (int)((g.M + 127) / 128);
         p.tilesN = (int)((g.N + 31) / 32);
+        if (g.b_lower) p.tilesN = (p.tilesN + 1) / 2;  // folded column blocks
         grid = dim3((unsigned)(p.tilesM * p.tilesN), grid.y);
         if (g.b_lower)
             hipLaunchKernelGGL((gemm_lf_kernel<RING, 1, false, false, true, true>), grid, dim3(256), 0, st, p);
@@ -1569,6 +1582,7 @@ hipError_t launch_lf_batched_cplx(const GemmDesc &g, hipStream_t st) {
     } else {
         p.tilesM = (int)((p.M + 127) / 128);
         p.tilesN = (int)((p.N + 31) / 32);
+        if (g.b_lower) p.tilesN = (p.tilesN + 1) / 2;  // folded column blocks
         grid = dim3((unsigned)(p.tilesM * p.tilesN), grid.y);
         if (g.b_lower)
             hipLaunchKernelGGL((gemm_lf_kernel<RING, 1, false, true, true, true>), grid, dim3(256), 0, st, p);
