@@ -101,6 +101,24 @@ __device__ __forceinline__ void st_elem(__amdgpu_buffer_rsrc_t r, int64_t idx, b
 // read and written with branch-free buffer operations, all in flight
 // together (a guarded access per element makes the compiler wait for each
 // one before the next).
+// v from lane r of this lane's quad (DPP quad permute; r must fold to a
+// constant)
+__device__ __forceinline__ int quad_bcast_w(int v, int r) {
+    switch (r) {
+    case 0: return __builtin_amdgcn_mov_dpp(v, 0x00, 0xF, 0xF, false);
+    case 1: return __builtin_amdgcn_mov_dpp(v, 0x55, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_mov_dpp(v, 0xAA, 0xF, 0xF, false);
+    default: return __builtin_amdgcn_mov_dpp(v, 0xFF, 0xF, 0xF, false);
+    }
+}
+template <typename T> __device__ __forceinline__ T quad_bcast(T v, int r) {
+    struct Words { int w[sizeof(T) / 4]; };
+    Words a = __builtin_bit_cast(Words, v);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) a.w[i] = quad_bcast_w(a.w[i], r);
+    return __builtin_bit_cast(T, a);
+}
+
 template <typename T, bool BUF>
 __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64_t ncg,
                                                          Scalar alpha_s, const T *__restrict__ A,
@@ -125,9 +143,8 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
 
     // ---- 1. this wave's 16 columns, all rows, into accumulators ----------
     // B does not depend on L, so its loads are in flight while L is staged
-    // and inverted (measured faster than loading B after the inversion,
-    // although the longer register life leaves three waves per SIMD for
-    // complex instead of four).  With buffer loads they are issued right
+    // and inverted (measured faster than loading B after the inversion).
+    // With buffer loads they are issued right
     // after L's: loads complete in order, so waiting for L then leaves B in
     // flight, and panel p of the solve below waits only for its own rows.
     const int64_t col = cgi * 64 + w * 16 + c;
@@ -215,24 +232,31 @@ __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64
     }
     __syncthreads();
 
-    // ---- 3. wave 0 inverts the diagonal blocks in place --------------------
-    // Lane group g takes block g, lane c of it column c of the inverse.  The
-    // pivots' reciprocals are computed first (one per lane) and stored over
-    // the diagonal, so the substitution itself only multiplies.
-    if (w == 0 && g < np) {
-        T(*D)[16] = Lb[blk(g, g)];
-        D[c][c] = E::recip(D[c][c]);
-        T x[16];
+    // ---- 3. the diagonal blocks are inverted in place, block w by wave w ---
+    // Lane 4c + r takes column c of the inverse, rows r, r + 4, r + 8 and
+    // r + 12, so each column is spread over one lane quad.  The pivots'
+    // reciprocals are stored over the diagonal first.  At step k the lane
+    // that holds row k scales it by the reciprocal, a quad permute hands the
+    // scaled value to the quad's other lanes, and each lane subtracts its
+    // multiples of it from its rows below k.
+    if (w < np) {
+        const int ic = lane >> 2, ir = lane & 3;
+        T(*D)[16] = Lb[blk(w, w)];
+        if (ir == 0) D[ic][ic] = E::recip(D[ic][ic]);
+        T x[4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == c) ? E::one() : E::zero();
+        for (int j = 0; j < 4; ++j) x[j] = (4 * j + ir == ic) ? E::one() : E::zero();
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            x[k] = E::mul(x[k], D[k][k]);
+            const int jk = k >> 2, rk = k & 3;
+            const T xk = quad_bcast(E::mul(x[jk], D[k][k]), rk);
+            const T u = E::msub(x[jk], D[k][4 * jk + ir], xk);
+            x[jk] = E::sel(ir > rk, u, E::sel(ir == rk, xk, x[jk]));
 #pragma unroll
-            for (int i = k + 1; i < 16; ++i) x[i] = E::msub(x[i], D[k][i], x[k]);
+            for (int j = jk + 1; j < 4; ++j) x[j] = E::msub(x[j], D[k][4 * j + ir], xk);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) D[c][i] = x[i];
+        for (int j = 0; j < 4; ++j) D[ic][4 * j + ir] = x[j];
     }
     __syncthreads();
 
