@@ -97,10 +97,6 @@ __device__ __forceinline__ void st_elem(__amdgpu_buffer_rsrc_t r, int64_t idx, b
     }
 }
 
-// BUF: one problem's A and B each span less than 2^31 bytes, so they are
-// read and written with branch-free buffer operations, all in flight
-// together (a guarded access per element makes the compiler wait for each
-// one before the next).
 // v from lane r of this lane's quad (DPP quad permute; r must fold to a
 // constant)
 __device__ __forceinline__ int quad_bcast_w(int v, int r) {
@@ -119,6 +115,10 @@ template <typename T> __device__ __forceinline__ T quad_bcast(T v, int r) {
     return __builtin_bit_cast(T, a);
 }
 
+// BUF: one problem's A and B each span less than 2^31 bytes, so they are
+// read and written with branch-free buffer operations, all in flight
+// together (a guarded access per element makes the compiler wait for each
+// one before the next).
 template <typename T, bool BUF>
 __global__ __launch_bounds__(256) void small_mfma_kernel(int m, int64_t n, int64_t ncg,
                                                          Scalar alpha_s, const T *__restrict__ A,
