@@ -104,9 +104,16 @@ lib = _load()
 
 # ---- marshalling helpers ---------------------------------------------------
 
+_DTYPE_CODES = None
+
+
 def _dtype_code(t) -> int:
-    import torch
-    code = {torch.float32: R32F, torch.float64: R64F, torch.complex128: C64F, torch.complex64: C32F}.get(t.dtype)
+    global _DTYPE_CODES
+    if _DTYPE_CODES is None:
+        import torch
+        _DTYPE_CODES = {torch.float32: R32F, torch.float64: R64F, torch.complex128: C64F,
+                        torch.complex64: C32F}
+    code = _DTYPE_CODES.get(t.dtype)
     if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}; use float32, float64, complex64 or complex128")
     return code
@@ -125,9 +132,22 @@ def alpha_buffer(code: int, alpha):
     return (ctypes.c_double * 2)(a.real, a.imag)
 
 
-def _stream_handle(stream) -> int:
-    import torch
+_RAW_STREAM = None
+
+
+def _stream_handle(stream, dev: int = None) -> int:
+    """The stream argument of a call: the given torch stream (or raw handle),
+    else torch's current stream, on device `dev` when the caller has already
+    established it (its raw handle is read without building a Stream object,
+    a few microseconds per call on a small solve)."""
+    global _RAW_STREAM
     if stream is None:
+        import torch
+        if dev is not None:
+            if _RAW_STREAM is None:
+                _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", False)
+            if _RAW_STREAM:
+                return int(_RAW_STREAM(dev))
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -147,25 +167,30 @@ def _check_device(where: str, *tensors, stream=None):
     """Every operand must be a tensor in GPU memory, all on one device, and
     an explicit torch stream must belong to that device: the library takes
     raw device pointers, and a host pointer reaching a kernel faults the GPU.
-    Raises before anything is handed to the library."""
+    Raises before anything is handed to the library.  Returns the device
+    index (None when every operand is None)."""
     dev = None
     for t in tensors:
         if t is None:
             continue
         if not getattr(t, "is_cuda", False):
-            raise ValueError(f"{where}: every operand must be a GPU tensor (got one on {t.device})")
+            raise ValueError(f"{where}: every operand must be a GPU tensor "
+                             f"(got one on {getattr(t, 'device', type(t).__name__)})")
+        d = t.get_device()
         if dev is None:
-            dev = t.device
-        elif t.device != dev:
-            raise ValueError(f"{where}: operands on different devices ({dev} and {t.device})")
+            dev = d
+        elif d != dev:
+            raise ValueError(f"{where}: operands on different devices (cuda:{dev} and cuda:{d})")
     sdev = getattr(stream, "device", None)
-    if dev is not None and sdev is not None and sdev != dev:
-        raise ValueError(f"{where}: stream on {sdev} but operands on {dev}")
+    if dev is not None and sdev is not None and sdev.index != dev:
+        raise ValueError(f"{where}: stream on {sdev} but operands on cuda:{dev}")
     if dev is not None:
         import torch
-        if torch.cuda.current_device() != dev.index:
-            raise ValueError(f"{where}: operands on {dev} but the current device is "
-                             f"cuda:{torch.cuda.current_device()} (use torch.cuda.device)")
+        cur = torch.cuda.current_device()
+        if cur != dev:
+            raise ValueError(f"{where}: operands on cuda:{dev} but the current device is "
+                             f"cuda:{cur} (use torch.cuda.device)")
+    return dev
 
 
 def _check(status: int, where: str):
@@ -193,10 +218,10 @@ def trsm_lln(A, B, alpha=1.0, *, stream=None):
     if tuple(A.shape) != (m, m):
         raise ValueError(f"A must be {m} x {m}")
     lda, ldb = _ld(A, m, m), _ld(B, m, n)
-    _check_device("trsm_lln", A, B, stream=stream)
+    dev = _check_device("trsm_lln", A, B, stream=stream)
     al = alpha_buffer(code, alpha)
     st = lib.trsm_lln(code, m, n, ctypes.addressof(al), A.data_ptr(), lda, B.data_ptr(), ldb,
-                      _stream_handle(stream))
+                      _stream_handle(stream, dev))
     _check(st, "trsm_lln")
     return B
 
@@ -216,10 +241,10 @@ def trsm_lln_noalloc(A, B, alpha=1.0, *, stream=None):
     if tuple(A.shape) != (m, m):
         raise ValueError(f"A must be {m} x {m}")
     lda, ldb = _ld(A, m, m), _ld(B, m, n)
-    _check_device("trsm_lln_noalloc", A, B, stream=stream)
+    dev = _check_device("trsm_lln_noalloc", A, B, stream=stream)
     al = alpha_buffer(code, alpha)
     st = lib.trsm_lln_noalloc(code, m, n, ctypes.addressof(al), A.data_ptr(), lda, B.data_ptr(), ldb,
-                              _stream_handle(stream))
+                              _stream_handle(stream, dev))
     _check(st, "trsm_lln_noalloc")
     return B
 
@@ -239,10 +264,10 @@ def trsm_solve(A, B, alpha=1.0, *, side="L", uplo="L", trans="N", diag="N", stre
     flags = ({"L": 0, "R": 1}[side], {"L": 0, "U": 1}[uplo], {"N": 0, "T": 1, "C": 2}[trans],
              {"N": 0, "U": 1}[diag])
     lda, ldb = _ld(A, k, k), _ld(B, m, n)
-    _check_device("trsm_solve", A, B, stream=stream)
+    dev = _check_device("trsm_solve", A, B, stream=stream)
     al = alpha_buffer(code, alpha)
     st = lib.trsm_solve(*flags, code, m, n, ctypes.addressof(al), A.data_ptr(), lda,
-                        B.data_ptr(), ldb, _stream_handle(stream))
+                        B.data_ptr(), ldb, _stream_handle(stream, dev))
     _check(st, "trsm_solve")
     return B
 
@@ -257,10 +282,10 @@ def trsm_lln_ex(A, B, alpha=1.0, ib: int = 0, force_blocked: bool = False, *, st
     if tuple(A.shape) != (m, m):
         raise ValueError(f"A must be {m} x {m}")
     lda, ldb = _ld(A, m, m), _ld(B, m, n)
-    _check_device("trsm_lln_ex", A, B, stream=stream)
+    dev = _check_device("trsm_lln_ex", A, B, stream=stream)
     al = alpha_buffer(code, alpha)
     st = lib.trsm_lln_ex(code, m, n, ctypes.addressof(al), A.data_ptr(), lda, B.data_ptr(), ldb,
-                         int(ib), int(bool(force_blocked)), _stream_handle(stream))
+                         int(ib), int(bool(force_blocked)), _stream_handle(stream, dev))
     _check(st, "trsm_lln_ex")
     return B
 
@@ -275,11 +300,11 @@ def trsm_lln_strided_batched(A, B, alpha=1.0, *, stream=None):
     if tuple(A.shape) != (batch, m, m):
         raise ValueError(f"A must be {batch} x {m} x {m}")
     lda, ldb = _ld(A, m, m), _ld(B, m, n)
-    _check_device("trsm_lln_strided_batched", A, B, stream=stream)
+    dev = _check_device("trsm_lln_strided_batched", A, B, stream=stream)
     al = alpha_buffer(code, alpha)
     st = lib.trsm_lln_strided_batched(code, m, n, ctypes.addressof(al), A.data_ptr(), lda,
                                       A.stride(0) if batch > 1 else 0, B.data_ptr(), ldb,
-                                      B.stride(0) if batch > 1 else 0, batch, _stream_handle(stream))
+                                      B.stride(0) if batch > 1 else 0, batch, _stream_handle(stream, dev))
     _check(st, "trsm_lln_strided_batched")
     return B
 
@@ -312,9 +337,9 @@ def trsm_kernel_diag_inv(A, W, ib: int, *, stream=None):
     nb = (m + ib - 1) // ib
     if W.dtype != A.dtype or W.numel() < nb * ib * ib or not W.is_contiguous():
         raise ValueError("W must be a contiguous buffer of ceil(m/ib)*ib*ib elements of A's dtype")
-    _check_device("trsm_kernel_diag_inv", A, W, stream=stream)
+    dev = _check_device("trsm_kernel_diag_inv", A, W, stream=stream)
     st = lib.trsm_kernel_diag_inv(code, int(ib), m, A.data_ptr(), _ld(A, m, m), W.data_ptr(),
-                                  _stream_handle(stream))
+                                  _stream_handle(stream, dev))
     _check(st, "trsm_kernel_diag_inv")
     return W
 
@@ -328,7 +353,7 @@ def trsm_kernel_gemm(A, Bm, D, *, beta=0.0, gamma=1.0, C=None, D2=None, split: i
     K2, N = Bm.shape
     if K2 != K or tuple(D.shape) != (M, N):
         raise ValueError("shape mismatch")
-    _check_device("trsm_kernel_gemm", A, Bm, D, C, D2, stream=stream)
+    dev = _check_device("trsm_kernel_gemm", A, Bm, D, C, D2, stream=stream)
     b = alpha_buffer(code, beta)
     g = alpha_buffer(code, gamma)
     c_ptr = C.data_ptr() if C is not None else None
@@ -338,7 +363,7 @@ def trsm_kernel_gemm(A, Bm, D, *, beta=0.0, gamma=1.0, C=None, D2=None, split: i
     st = lib.trsm_kernel_gemm(code, M, N, K, ctypes.addressof(b), ctypes.addressof(g),
                               A.data_ptr(), _ld(A, M, K), Bm.data_ptr(), _ld(Bm, K, N),
                               c_ptr, ldc, D.data_ptr(), _ld(D, M, N), d2_ptr, ldd2,
-                              int(split), int(bool(a_lower)), _stream_handle(stream))
+                              int(split), int(bool(a_lower)), _stream_handle(stream, dev))
     _check(st, "trsm_kernel_gemm")
     return D
 
