@@ -469,6 +469,22 @@ def test_non_default_stream(T):
     check("f64", from_dev(Bd), oracle.solve(L, B, 1.0), "side stream")
 
 
+def test_current_stream_is_used(T):
+    """With no stream argument a call goes to torch's current stream (the
+    binding reads its raw handle for the operands' device)."""
+    import torch
+    dev = torch.cuda.current_device()
+    L, B = make_problem("f64", 500, 100, seed=4)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert T._stream_handle(None, dev) == s.cuda_stream
+        Ad, Bd = to_dev(L), to_dev(B)
+        T.trsm_lln(Ad, Bd, 1.0)
+    s.synchronize()
+    check("f64", from_dev(Bd), oracle.solve(L, B, 1.0), "current stream")
+    assert T._stream_handle(None, dev) == torch.cuda.current_stream().cuda_stream
+
+
 def test_workspace_allocation_failure_leaves_B_untouched(T, monkeypatch):
     import torch
     L, B = make_problem("f64", 300, 40, seed=9)
