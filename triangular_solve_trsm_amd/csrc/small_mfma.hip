@@ -16,9 +16,9 @@
 //     and B moves by a raw buffer operation with no branch around it, so all
 //     of a thread's loads are in flight at once and its stores go out
 //     back to back (guarded loads made the compiler wait for each one);
-//   * one wave inverts the four diagonal blocks in place (lane group g takes
-//     block g) by substitution against the columns of the identity (section
-//     4.3.1's column-streamed inversion at 16 x 16 scale);
+//   * wave w inverts diagonal block w in place by substitution against the
+//     columns of the identity (section 4.3.1's column-streamed inversion at
+//     16 x 16 scale), each column spread over a lane quad;
 //   * wave w then owns right-hand-side columns 16w .. 16w+15 of the group,
 //     all 64 rows of them as v_mfma_f64_16x16x4f64 accumulators, and for
 //     p = 0..3 computes X_p = W_p B_p and B_q -= L_qp X_p (q > p) without
@@ -28,8 +28,8 @@
 //   * complex fp64 uses the real 2x2 embedding (4 real products per complex
 //     product), expanded from the complex LDS blocks when the A fragments
 //     are read.
-// Four waves per workgroup and three (complex) or four (fp64) workgroups
-// per CU, so one workgroup's loads overlap the others' products.
+// Four waves per workgroup and three (complex, by registers) or six (fp64)
+// workgroups per CU, so one workgroup's loads overlap the others' products.
 #include <cstdlib>
 #include <map>
 #include <mutex>
