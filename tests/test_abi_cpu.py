@@ -217,6 +217,47 @@ def test_python_binding_rejects_host_tensors(T):
             call_()
 
 
+class _FakeGpuTensor:
+    """Stands in for a GPU tensor in the binding's device checks (no GPU
+    here): only is_cuda, get_device() and device are read."""
+
+    def __init__(self, index):
+        import torch
+        self.is_cuda = True
+        self._index = index
+        self.device = torch.device("cuda", index)
+
+    def get_device(self):
+        return self._index
+
+
+class _FakeStream:
+    def __init__(self, index):
+        import torch
+        self.device = torch.device("cuda", index)
+
+
+def test_device_checks_refuse_mixed_devices(T, monkeypatch):
+    """The binding's device checks with integer device indices: operands on
+    two devices, operands off the current device and a stream on another
+    device are refused; matching operands give their device index; no
+    operand gives None."""
+    import torch
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 0)
+    a0, a1 = _FakeGpuTensor(0), _FakeGpuTensor(1)
+    assert T._check_device("t", a0, a0, None) == 0
+    assert T._check_device("t", None, None) is None
+    with pytest.raises(ValueError, match="different devices"):
+        T._check_device("t", a0, a1)
+    with pytest.raises(ValueError, match="current device"):
+        T._check_device("t", a1, a1)
+    with pytest.raises(ValueError, match="stream on"):
+        T._check_device("t", a0, a0, stream=_FakeStream(1))
+    assert T._check_device("t", a0, stream=_FakeStream(0)) == 0
+    with pytest.raises(ValueError, match="GPU tensor"):
+        T._check_device("t", a0, torch.zeros(2))
+
+
 def test_noalloc_refuses_before_any_hip_call(T):
     """trsm_lln_noalloc checks its arguments like trsm_lln, and refuses a
     problem whose blocked-path workspace exceeds its fixed scratch array
